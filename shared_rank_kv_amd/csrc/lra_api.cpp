@@ -1,0 +1,429 @@
+// C-ABI front end of liblra.so: argument validation (host only, before any HIP call),
+// work planning, workspace sizing and kernel dispatch.  Declarations and the contract of
+// every entry point are in include/lra.h.
+#include "lra.h"
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
+#include "lra_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return LRA_OK;
+}
+
+bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int env_int(const char* name, int dflt) {
+  const char* v = std::getenv(name);
+  if (!v || !*v) return dflt;
+  int x = std::atoi(v);
+  return x > 0 ? x : dflt;
+}
+
+// ---------------------------------------------------------------------------------------
+// Validation
+// ---------------------------------------------------------------------------------------
+
+struct AttnShape {
+  int dtype, batch, Hq, Hkv, D;
+};
+
+int check_shape(const AttnShape& s) {
+  if (s.dtype != LRA_DTYPE_F32 && s.dtype != LRA_DTYPE_BF16)
+    return fail(LRA_ERR_INVALID, "dtype %d is neither LRA_DTYPE_F32 nor LRA_DTYPE_BF16", s.dtype);
+  if (s.batch < 0) return fail(LRA_ERR_INVALID, "batch %d < 0", s.batch);
+  if (s.batch > LRA_MAX_BATCH)
+    return fail(LRA_ERR_UNSUPPORTED, "batch %d > LRA_MAX_BATCH (%d)", s.batch, LRA_MAX_BATCH);
+  if (s.Hq <= 0 || s.Hkv <= 0)
+    return fail(LRA_ERR_INVALID, "head counts must be positive (n_q_heads %d, n_kv_heads %d)",
+                s.Hq, s.Hkv);
+  if (s.Hq % s.Hkv != 0)
+    return fail(LRA_ERR_INVALID, "n_q_heads %d is not a multiple of n_kv_heads %d", s.Hq, s.Hkv);
+  if (s.Hq / s.Hkv > LRA_MAX_GROUP)
+    return fail(LRA_ERR_UNSUPPORTED, "group size %d > LRA_MAX_GROUP (%d)", s.Hq / s.Hkv,
+                LRA_MAX_GROUP);
+  if (s.D <= 0) return fail(LRA_ERR_INVALID, "head_dim %d <= 0", s.D);
+  if (s.D != 64 && s.D != 128)
+    return fail(LRA_ERR_UNSUPPORTED, "head_dim %d not in {64, 128}", s.D);
+  return LRA_OK;
+}
+
+struct Adapters {
+  int32_t n_agents;
+  const int32_t* ranks;
+  const void* const* L;
+  const int64_t* ldl;
+  const void* const* B;
+};
+
+int check_adapters(int dtype, const Adapters& ad, int64_t kv_rows) {
+  if (ad.n_agents <= 0) return fail(LRA_ERR_INVALID, "n_agents %d <= 0", ad.n_agents);
+  if (ad.n_agents > LRA_MAX_AGENTS)
+    return fail(LRA_ERR_UNSUPPORTED, "n_agents %d > LRA_MAX_AGENTS (%d)", ad.n_agents,
+                LRA_MAX_AGENTS);
+  if (!ad.ranks || !ad.L || !ad.ldl || !ad.B)
+    return fail(LRA_ERR_INVALID, "ranks, L, ldl and B must be non-null host arrays");
+  const int ldl_mult = dtype == LRA_DTYPE_BF16 ? 8 : 4;
+  for (int a = 0; a < ad.n_agents; ++a) {
+    const int r = ad.ranks[a];
+    if (r < 0) return fail(LRA_ERR_INVALID, "ranks[%d] = %d < 0", a, r);
+    if (r > LRA_MAX_RANK || r % 8 != 0)
+      return fail(LRA_ERR_UNSUPPORTED, "ranks[%d] = %d: ranks must be multiples of 8 up to %d",
+                  a, r, LRA_MAX_RANK);
+    if (r == 0) continue;
+    if (!ad.L[a] || !ad.B[a]) return fail(LRA_ERR_INVALID, "L[%d] / B[%d] is null", a, a);
+    if (ad.ldl[a] < r) return fail(LRA_ERR_INVALID, "ldl[%d] = %lld < rank %d", a,
+                                   (long long)ad.ldl[a], r);
+    if (ad.ldl[a] % ldl_mult != 0)
+      return fail(LRA_ERR_INVALID, "ldl[%d] = %lld is not a multiple of %d elements", a,
+                  (long long)ad.ldl[a], ldl_mult);
+    if (!aligned(ad.L[a], 16) || !aligned(ad.B[a], 16))
+      return fail(LRA_ERR_INVALID, "L[%d] / B[%d] not 16-byte aligned", a, a);
+    (void)kv_rows;
+  }
+  return LRA_OK;
+}
+
+struct Requests {
+  const int32_t* q_start;
+  const int32_t* q_len;
+  const int32_t* k_start;
+  const int32_t* k_len;
+  const int32_t* agent;
+};
+
+int check_requests(int batch, const Requests& rq, int64_t q_rows, int64_t kv_rows,
+                   int32_t n_agents) {
+  if (batch == 0) return LRA_OK;
+  if (!rq.q_start || !rq.q_len || !rq.k_start || !rq.k_len || !rq.agent)
+    return fail(LRA_ERR_INVALID, "request arrays must be non-null host arrays");
+  if (q_rows < 0 || kv_rows < 0) return fail(LRA_ERR_INVALID, "q_rows / kv_rows < 0");
+  std::vector<std::pair<int64_t, int64_t>> spans;
+  for (int b = 0; b < batch; ++b) {
+    const int64_t qs = rq.q_start[b], ql = rq.q_len[b], ks = rq.k_start[b], kl = rq.k_len[b];
+    if (ql < 0 || kl < 0) return fail(LRA_ERR_INVALID, "request %d: negative length", b);
+    if (ql == 0) continue;
+    if (ql > kl)
+      return fail(LRA_ERR_INVALID, "request %d: q_len %lld > k_len %lld", b, (long long)ql,
+                  (long long)kl);
+    if (qs < 0 || qs + ql > q_rows)
+      return fail(LRA_ERR_INVALID, "request %d: query rows [%lld, %lld) outside [0, %lld)", b,
+                  (long long)qs, (long long)(qs + ql), (long long)q_rows);
+    if (ks < 0 || ks + kl > kv_rows)
+      return fail(LRA_ERR_INVALID, "request %d: key rows [%lld, %lld) outside [0, %lld)", b,
+                  (long long)ks, (long long)(ks + kl), (long long)kv_rows);
+    if (rq.agent[b] < 0 || rq.agent[b] >= n_agents)
+      return fail(LRA_ERR_INVALID, "request %d: agent_idx %d outside [0, %d)", b, rq.agent[b],
+                  n_agents);
+    spans.emplace_back(qs, qs + ql);
+  }
+  std::sort(spans.begin(), spans.end());
+  for (size_t i = 1; i < spans.size(); ++i)
+    if (spans[i].first < spans[i - 1].second)
+      return fail(LRA_ERR_INVALID, "query/output rows of two requests overlap at row %lld",
+                  (long long)spans[i].first);
+  return LRA_OK;
+}
+
+// ---------------------------------------------------------------------------------------
+// Planning (deterministic: the workspace query and the call agree)
+// ---------------------------------------------------------------------------------------
+
+struct Plan {
+  std::vector<int> active;     // requests with q_len > 0, in order
+  std::vector<int> n_rt, n_split;
+  std::vector<int64_t> part_base;
+  int64_t part_rows = 0;
+  size_t ws_bytes = 0;
+};
+
+constexpr int kPartCols = 64;          // ws_l columns (maximum rank)
+
+size_t part_bytes(int64_t part_rows, int D) {
+  return (size_t)part_rows * (size_t)(D + kPartCols + 2) * sizeof(float);
+}
+
+Plan make_plan(const AttnShape& s, bool decode, const int32_t* q_len, const int32_t* k_len) {
+  Plan p;
+  const int G = s.Hq / s.Hkv;
+  for (int b = 0; b < s.batch; ++b) {
+    const int ql = decode ? 1 : q_len[b];
+    if (ql <= 0) continue;
+    p.active.push_back(b);
+  }
+  const size_t n = p.active.size();
+  p.n_rt.resize(n);
+  p.n_split.assign(n, 1);
+  p.part_base.assign(n, -1);
+  if (s.dtype == LRA_DTYPE_F32) {
+    for (size_t i = 0; i < n; ++i) {
+      const int ql = decode ? 1 : q_len[p.active[i]];
+      p.n_rt[i] = (int)ceil_div(ql, 64);
+    }
+    return p;
+  }
+  int64_t total_wg = 0;
+  for (size_t i = 0; i < n; ++i) {
+    const int ql = decode ? 1 : q_len[p.active[i]];
+    p.n_rt[i] = (int)ceil_div((int64_t)ql * G, lra::kTileRows);
+    total_wg += (int64_t)s.Hkv * p.n_rt[i];
+  }
+  if (decode) {
+    const int chunk = env_int("LRA_DECODE_CHUNK", 1024);
+    for (size_t i = 0; i < n; ++i) {
+      const int64_t kl = k_len[p.active[i]];
+      const int64_t tiles = ceil_div(kl, lra::kTileKeys);
+      p.n_split[i] = (int)std::max<int64_t>(1, std::min<int64_t>({ceil_div(kl, chunk), tiles, 64}));
+    }
+  } else {
+    const int target = env_int("LRA_PREFILL_TARGET_WG", 512);
+    if (total_wg < target) {
+      const int64_t factor = ceil_div(target, std::max<int64_t>(total_wg, 1));
+      for (size_t i = 0; i < n; ++i) {
+        const int64_t tiles = ceil_div(k_len[p.active[i]], lra::kTileKeys);
+        p.n_split[i] = (int)std::max<int64_t>(1, std::min<int64_t>({factor, tiles / 8, 64}));
+      }
+    }
+  }
+  for (size_t i = 0; i < n; ++i) {
+    if (p.n_split[i] <= 1) continue;
+    const int ql = decode ? 1 : q_len[p.active[i]];
+    p.part_base[i] = p.part_rows;
+    p.part_rows += (int64_t)p.n_split[i] * ql * s.Hq;
+  }
+  p.ws_bytes = p.part_rows ? part_bytes(p.part_rows, s.D) + 256 : 0;
+  return p;
+}
+
+// ---------------------------------------------------------------------------------------
+// Dispatch
+// ---------------------------------------------------------------------------------------
+
+int run_attention(const AttnShape& s, bool decode, const Requests& rq, const void* Q,
+                  const void* K, const void* V, const Adapters& ad, void* O, void* ws,
+                  size_t ws_bytes, hipStream_t stream) {
+  const int32_t* q_len_arg = decode ? nullptr : rq.q_len;
+  Plan p = make_plan(s, decode, q_len_arg, rq.k_len);
+  if (p.active.empty()) return ok();
+  if (p.ws_bytes > 0) {
+    if (!ws) return fail(LRA_ERR_WORKSPACE, "workspace is null; %zu bytes needed", p.ws_bytes);
+    if (ws_bytes < p.ws_bytes)
+      return fail(LRA_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, p.ws_bytes);
+  }
+  const int G = s.Hq / s.Hkv;
+  lra::AttnArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.Q = Q;
+  a.K = K;
+  a.V = V;
+  a.O = O;
+  if (p.part_rows) {
+    uintptr_t base = (reinterpret_cast<uintptr_t>(ws) + 255) & ~uintptr_t(255);
+    a.ws_o = reinterpret_cast<float*>(base);
+    a.ws_l = a.ws_o + p.part_rows * s.D;
+    a.ws_ml = a.ws_l + p.part_rows * kPartCols;
+  }
+  a.Hq = s.Hq;
+  a.Hkv = s.Hkv;
+  a.G = G;
+  a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)s.D));
+  for (int i = 0; i < ad.n_agents; ++i) {
+    a.agents[i].L = ad.L[i];
+    a.agents[i].B = ad.B[i];
+    a.agents[i].ldl = ad.ldl[i];
+    a.agents[i].rank = ad.ranks[i];
+  }
+  const size_t n = p.active.size();
+  for (size_t c0 = 0; c0 < n; c0 += lra::kReqsPerLaunch) {
+    const size_t c1 = std::min(n, c0 + lra::kReqsPerLaunch);
+    int64_t work = 0, comb = 0;
+    a.n_req = (int)(c1 - c0);
+    for (size_t i = c0; i < c1; ++i) {
+      const int b = p.active[i];
+      lra::ReqDesc& r = a.reqs[i - c0];
+      r.q_start = decode ? b : rq.q_start[b];
+      r.q_len = decode ? 1 : rq.q_len[b];
+      r.k_start = rq.k_start[b];
+      r.k_len = rq.k_len[b];
+      r.agent = rq.agent[b];
+      r.n_rt = p.n_rt[i];
+      r.n_split = p.n_split[i];
+      r.work_start = (int)work;
+      r.part_base = (int)p.part_base[i];
+      r.comb_start = (int)comb;
+      const int heads_per_item = s.dtype == LRA_DTYPE_F32 ? s.Hq : s.Hkv;
+      work += (int64_t)heads_per_item * r.n_rt * r.n_split;
+      if (r.n_split > 1) comb += (int64_t)r.q_len * s.Hq;
+    }
+    if (work > INT32_MAX / 2) return fail(LRA_ERR_UNSUPPORTED, "launch too large");
+    a.n_work = (int)work;
+    a.n_comb = (int)comb;
+    hipError_t e;
+    if (s.dtype == LRA_DTYPE_BF16) {
+      const int grid = (int)ceil_div(work, 8) * 8;
+      a.grid_per_xcd = grid / 8;
+      e = lra::launch_attn_bf16(a, s.D, grid, stream);
+      if (e == hipSuccess && comb > 0) e = lra::launch_combine_bf16(a, s.D, stream);
+    } else {
+      a.grid_per_xcd = 0;
+      e = lra::launch_attn_f32(a, s.D, (int)work, stream);
+    }
+    if (e != hipSuccess) return fail(LRA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  }
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* lra_last_error(void) { return g_err; }
+
+size_t lra_attn_workspace_bytes(int dtype, int is_decode, int32_t batch, const int32_t* q_len,
+                                const int32_t* k_len, int32_t n_q_heads, int32_t n_kv_heads,
+                                int32_t head_dim, int32_t max_rank) {
+  AttnShape s{dtype, batch, n_q_heads, n_kv_heads, head_dim};
+  if (check_shape(s) != LRA_OK) return (size_t)-1;
+  if (max_rank < 0 || max_rank > LRA_MAX_RANK) return (size_t)-1;
+  if (batch > 0 && (!k_len || (!is_decode && !q_len))) return (size_t)-1;
+  for (int b = 0; b < batch; ++b) {
+    if (k_len[b] < 0 || (!is_decode && (q_len[b] < 0 || q_len[b] > k_len[b]))) return (size_t)-1;
+    if (is_decode && k_len[b] < 1) return (size_t)-1;
+  }
+  return make_plan(s, is_decode != 0, q_len, k_len).ws_bytes;
+}
+
+int lra_attn_prefill(int dtype, int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                     int32_t head_dim, const int32_t* q_start, const int32_t* q_len,
+                     const int32_t* k_start, const int32_t* k_len, const int32_t* agent_idx,
+                     const void* Q, int64_t q_rows, const void* K_base, const void* V_base,
+                     int64_t kv_rows, int32_t n_agents, const int32_t* ranks,
+                     const void* const* L, const int64_t* ldl, const void* const* B, void* O,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  AttnShape s{dtype, batch, n_q_heads, n_kv_heads, head_dim};
+  int rc = check_shape(s);
+  if (rc) return rc;
+  Adapters ad{n_agents, ranks, L, ldl, B};
+  if ((rc = check_adapters(dtype, ad, kv_rows))) return rc;
+  Requests rq{q_start, q_len, k_start, k_len, agent_idx};
+  if ((rc = check_requests(batch, rq, q_rows, kv_rows, n_agents))) return rc;
+  bool any = false;
+  for (int b = 0; b < batch; ++b) any |= q_len[b] > 0;
+  if (!any) return ok();
+  if (!Q || !K_base || !V_base || !O)
+    return fail(LRA_ERR_INVALID, "Q, K_base, V_base and O must be non-null");
+  if (!aligned(Q, 16) || !aligned(K_base, 16) || !aligned(V_base, 16) || !aligned(O, 16))
+    return fail(LRA_ERR_INVALID, "Q, K_base, V_base and O must be 16-byte aligned");
+  return run_attention(s, false, rq, Q, K_base, V_base, ad, O, workspace, workspace_bytes,
+                       (hipStream_t)stream);
+}
+
+int lra_attn_decode(int dtype, int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                    int32_t head_dim, const int32_t* k_start, const int32_t* k_len,
+                    const int32_t* agent_idx, const void* Q, const void* K_base,
+                    const void* V_base, int64_t kv_rows, int32_t n_agents, const int32_t* ranks,
+                    const void* const* L, const int64_t* ldl, const void* const* B, void* O,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  AttnShape s{dtype, batch, n_q_heads, n_kv_heads, head_dim};
+  int rc = check_shape(s);
+  if (rc) return rc;
+  Adapters ad{n_agents, ranks, L, ldl, B};
+  if ((rc = check_adapters(dtype, ad, kv_rows))) return rc;
+  if (batch == 0) return ok();
+  if (!k_start || !k_len || !agent_idx)
+    return fail(LRA_ERR_INVALID, "request arrays must be non-null host arrays");
+  std::vector<int32_t> qs(batch), ql(batch, 1);
+  for (int b = 0; b < batch; ++b) qs[b] = b;
+  Requests rq{qs.data(), ql.data(), k_start, k_len, agent_idx};
+  if ((rc = check_requests(batch, rq, batch, kv_rows, n_agents))) return rc;
+  if (!Q || !K_base || !V_base || !O)
+    return fail(LRA_ERR_INVALID, "Q, K_base, V_base and O must be non-null");
+  if (!aligned(Q, 16) || !aligned(K_base, 16) || !aligned(V_base, 16) || !aligned(O, 16))
+    return fail(LRA_ERR_INVALID, "Q, K_base, V_base and O must be 16-byte aligned");
+  return run_attention(s, true, rq, Q, K_base, V_base, ad, O, workspace, workspace_bytes,
+                       (hipStream_t)stream);
+}
+
+int lra_precompute_lr(int dtype, int64_t T, int64_t d_model, const void* X, int64_t ldx,
+                      const void* A_cat, int64_t lda, int32_t n_agents, const int32_t* ranks,
+                      void* const* L_out, const int64_t* ldl, void* stream) {
+  if (dtype != LRA_DTYPE_F32 && dtype != LRA_DTYPE_BF16)
+    return fail(LRA_ERR_INVALID, "dtype %d is neither LRA_DTYPE_F32 nor LRA_DTYPE_BF16", dtype);
+  if (T < 0 || d_model <= 0) return fail(LRA_ERR_INVALID, "T %lld < 0 or d_model %lld <= 0",
+                                         (long long)T, (long long)d_model);
+  if (n_agents <= 0) return fail(LRA_ERR_INVALID, "n_agents %d <= 0", n_agents);
+  if (n_agents > LRA_MAX_AGENTS)
+    return fail(LRA_ERR_UNSUPPORTED, "n_agents %d > LRA_MAX_AGENTS (%d)", n_agents, LRA_MAX_AGENTS);
+  if (!ranks || !L_out || !ldl) return fail(LRA_ERR_INVALID, "ranks, L_out, ldl must be non-null");
+  int64_t R = 0;
+  for (int a = 0; a < n_agents; ++a) {
+    if (ranks[a] < 0) return fail(LRA_ERR_INVALID, "ranks[%d] = %d < 0", a, ranks[a]);
+    if (ranks[a] > LRA_MAX_RANK || ranks[a] % 8 != 0)
+      return fail(LRA_ERR_UNSUPPORTED, "ranks[%d] = %d: ranks must be multiples of 8 up to %d", a,
+                  ranks[a], LRA_MAX_RANK);
+    if (ranks[a] > 0) {
+      if (!L_out[a]) return fail(LRA_ERR_INVALID, "L_out[%d] is null", a);
+      if (ldl[a] < ranks[a]) return fail(LRA_ERR_INVALID, "ldl[%d] < ranks[%d]", a, a);
+      if (!aligned(L_out[a], 4)) return fail(LRA_ERR_INVALID, "L_out[%d] not 4-byte aligned", a);
+    }
+    R += ranks[a];
+  }
+  if (d_model % 8 != 0) return fail(LRA_ERR_UNSUPPORTED, "d_model %lld %% 8 != 0", (long long)d_model);
+  if (ldx < d_model || ldx % 8 != 0)
+    return fail(LRA_ERR_INVALID, "ldx %lld must be >= d_model and a multiple of 8", (long long)ldx);
+  if (lda < R) return fail(LRA_ERR_INVALID, "lda %lld < sum of ranks %lld", (long long)lda,
+                           (long long)R);
+  if (T == 0 || R == 0) return ok();
+  if (!X || !A_cat) return fail(LRA_ERR_INVALID, "X and A_cat must be non-null");
+  if (!aligned(X, 16) || !aligned(A_cat, dtype == LRA_DTYPE_BF16 ? 16 : 4))
+    return fail(LRA_ERR_INVALID, "X must be 16-byte aligned, A_cat %d-byte aligned",
+                dtype == LRA_DTYPE_BF16 ? 16 : 4);
+  if (dtype == LRA_DTYPE_BF16 && (lda % 8 != 0))
+    return fail(LRA_ERR_INVALID, "lda %lld must be a multiple of 8 for bf16", (long long)lda);
+  if (R > 256) return fail(LRA_ERR_UNSUPPORTED, "sum of ranks %lld > 256", (long long)R);
+  lra::PrecomputeArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.X = X;
+  a.A = A_cat;
+  a.T = T;
+  a.d_model = d_model;
+  a.ldx = ldx;
+  a.lda = lda;
+  a.R = (int)R;
+  a.n_agents = n_agents;
+  int32_t off = 0;
+  for (int i = 0; i < n_agents; ++i) {
+    a.Lout[i] = L_out[i];
+    a.ldl[i] = ldl[i];
+    a.col_start[i] = off;
+    off += ranks[i];
+  }
+  a.col_start[n_agents] = off;
+  hipError_t e = dtype == LRA_DTYPE_BF16 ? lra::launch_precompute_bf16(a, (hipStream_t)stream)
+                                         : lra::launch_precompute_f32(a, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(LRA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,81 @@
+// Internal interface between the C-ABI front end (lra_api.cpp) and the HIP kernels.
+// Kernel arguments are passed by value; per-request and per-agent tables live inside the
+// argument block and kernels read them through the kernarg segment pointer, so nothing
+// has to be copied to device memory before a launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstddef>
+#include <cstdint>
+
+namespace lra {
+
+constexpr int kMaxAgents = 16;
+constexpr int kMaxRank = 64;
+constexpr int kReqsPerLaunch = 64;   // larger batches are split into several launches
+
+// Tile geometry of the bf16 attention kernel (see fla_bf16.hip).
+constexpr int kTileRows = 128;       // (query, head-in-group) rows per workgroup
+constexpr int kTileKeys = 64;        // keys per LDS tile
+constexpr int kThreads = 256;        // 4 waves of 64
+
+struct AgentDesc {
+  const void* L;      // [kv_rows, ldl] LR cache (device)
+  const void* B;      // [rank, Hkv*D] up-projection (device)
+  int64_t ldl;        // row stride of L in elements
+  int32_t rank;
+  int32_t pad_;
+};
+
+// One request of a launch.  Work items of a request are numbered
+// ((g * n_split + split) * n_rt + rt) with rt (row tile) fastest.
+struct ReqDesc {
+  int32_t q_start, q_len, k_start, k_len;
+  int32_t agent;
+  int32_t n_rt;        // row tiles per kv head
+  int32_t n_split;     // key-range splits (1: the attention kernel writes O directly)
+  int32_t work_start;  // first work item of this request within the launch
+  int32_t part_base;   // first partial row in the workspace (split requests), else -1
+  int32_t comb_start;  // first combine row of this request within the launch
+};
+
+struct AttnArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  void* O;
+  float* ws_o;         // [part_rows, D]      unnormalised P·V_base partials
+  float* ws_l;         // [part_rows, 64]     unnormalised P·L partials
+  float* ws_ml;        // [part_rows, 2]      (running max in log2 units, row sum)
+  int32_t Hq, Hkv, G;
+  int32_t n_req;
+  int32_t n_work;      // work items (workgroups that do work) in this launch
+  int32_t grid_per_xcd;
+  int32_t n_comb;      // combine rows in this launch
+  float scale_log2;    // log2(e) / sqrt(D)
+  AgentDesc agents[kMaxAgents];
+  ReqDesc reqs[kReqsPerLaunch];
+};
+
+// Precompute: L_a[t, :] = X[t, :] · A_cat[:, off_a : off_a + r_a].
+struct PrecomputeArgs {
+  const void* X;
+  const void* A;
+  int64_t T, d_model, ldx, lda;
+  int32_t R;           // total columns (sum of ranks)
+  int32_t n_agents;
+  int32_t n_row_tiles;
+  int32_t grid_per_xcd;
+  void* Lout[kMaxAgents];
+  int64_t ldl[kMaxAgents];
+  int32_t col_start[kMaxAgents + 1];
+};
+
+// Launchers (return the HIP status of the launch).
+hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, int n_grid, hipStream_t s);
+hipError_t launch_combine_bf16(const AttnArgs& a, int head_dim, hipStream_t s);
+hipError_t launch_attn_f32(const AttnArgs& a, int head_dim, int n_blocks, hipStream_t s);
+hipError_t launch_precompute_bf16(const PrecomputeArgs& a, hipStream_t s);
+hipError_t launch_precompute_f32(const PrecomputeArgs& a, hipStream_t s);
+
+}  // namespace lra

@@ -1,0 +1,195 @@
+"""GPU parity of the HIP path against the CPU fp64 oracle, element by element, at sizes the
+oracle finishes in seconds (several tiles, ragged tails, edge cases).  Calls go through the
+C ABI (ctypes binding); nothing here computes on the GPU other than liblra.so's kernels."""
+
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from shared_rank_kv_amd import workloads
+
+import helpers as H
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    from shared_rank_kv_amd import lra   # fails loudly if liblra.so is missing
+    assert torch.cuda.is_available()
+    return lra
+
+
+def _cmp_full(prob, cpu, O, bf16=True, what=None, rel_frob=H.REL_FROB):
+    rows = H.covered_rows(prob)
+    want = H.oracle_all(prob, cpu)[rows]
+    got = O.float().cpu().numpy()[rows]
+    what = what or prob.name
+    if bf16:
+        return H.assert_bf16_close(got, want, what, rel_frob)
+    return H.assert_f32_close(got, want, what)
+
+
+# ---------------------------------------------------------------------------------------
+# fp32 path
+# ---------------------------------------------------------------------------------------
+
+def test_tiny_fp32_both_agents():
+    prob = workloads.tiny_fp32()
+    cpu, dev = H.device_inputs(prob)
+    O = H.run_prefill(prob, dev)
+    mx, _, _ = _cmp_full(prob, cpu, O, bf16=False)
+    print(f"tiny fp32 max-abs {mx:.2e}")
+    # the LR term is far above the fp32 tolerance here, so this also pins it
+    lr_only = H.oracle_all(prob, cpu) - H.oracle_all(prob, {**cpu, "B": [torch.zeros_like(b) for b in cpu["B"]]})
+    assert np.abs(lr_only).max() > 100 * H.F32_MAX_ABS
+
+
+@pytest.mark.parametrize("D,Hq,Hkv", [(128, 8, 2), (64, 4, 4)])
+def test_fp32_ragged_batch(D, Hq, Hkv):
+    prob = workloads.custom("f32-ragged", "f32", Hq, Hkv, D, (16, 0, 64), q_len=[1, 70, 33],
+                            k_len=[9, 70, 190], agent_idx=[0, 1, 2], seed=501)
+    cpu, dev = H.device_inputs(prob)
+    _cmp_full(prob, cpu, H.run_prefill(prob, dev), bf16=False)
+
+
+def test_fp32_decode():
+    prob = workloads.custom("f32-decode", "f32", 8, 2, 128, (8, 32), q_len=[1, 1, 1],
+                            k_len=[1, 100, 700], agent_idx=[1, 0, 1], seed=502)
+    cpu, dev = H.device_inputs(prob)
+    O = H.run_decode(prob, dev)
+    _cmp_full(prob, cpu, O, bf16=False)
+
+
+# ---------------------------------------------------------------------------------------
+# bf16 path
+# ---------------------------------------------------------------------------------------
+
+BF16_SHAPES = [
+    # D, Hq, Hkv, ranks, q_len, k_len, agents
+    (128, 8, 2, (16, 64, 8, 0), [1, 37, 200, 64], [5, 300, 700, 64], [0, 1, 2, 3]),
+    (128, 32, 8, (16, 32), [130, 3], [450, 1000], [1, 0]),
+    (64, 4, 4, (24, 48), [100, 17], [333, 17], [0, 1]),
+    (128, 8, 1, (40,), [20, 9], [150, 9], [0, 0]),
+    (64, 16, 8, (8, 56), [64, 65], [128, 129], [1, 0]),
+]
+
+
+@pytest.mark.parametrize("shape", BF16_SHAPES, ids=[f"D{s[0]}-Hq{s[1]}-Hkv{s[2]}" for s in BF16_SHAPES])
+def test_bf16_ragged_batch(shape):
+    D, Hq, Hkv, ranks, q_len, k_len, agents = shape
+    prob = workloads.custom("bf16-ragged", "bf16", Hq, Hkv, D, ranks, q_len, k_len, agents,
+                            seed=600 + D + Hq)
+    cpu, dev = H.device_inputs(prob)
+    O = H.run_prefill(prob, dev)
+    _cmp_full(prob, cpu, O)
+
+
+def test_bf16_lr_isolated_and_peaked():
+    # V_base = 0 leaves only (P·L)·B, which the default tolerances would barely see.
+    prob = workloads.custom("bf16-lr-only", "bf16", 8, 2, 128, (16, 64), [50, 120], [400, 900],
+                            [0, 1], seed=610)
+    cpu, dev = H.device_inputs(prob, zero_v=True)
+    O = H.run_prefill(prob, dev)
+    mx, mean, rel = _cmp_full(prob, cpu, O, what="lr-only")
+    print(f"LR-isolated rel-frob {rel:.2e}")
+    cpu, dev = H.device_inputs(prob, q_scale=8.0)
+    _cmp_full(prob, cpu, H.run_prefill(prob, dev), what="peaked")
+
+
+def test_bf16_shared_context_and_shared_lr_cache():
+    # BaseShared: every request reads the same base rows; BaseLRShared: one LR cache for all.
+    prob = workloads.custom("bf16-shared", "bf16", 8, 2, 128, (16, 16, 16), [40, 40, 40],
+                            [500, 500, 500], [0, 1, 2], seed=620, shared_k=True)
+    cpu, dev = H.device_inputs(prob)
+    _cmp_full(prob, cpu, H.run_prefill(prob, dev))
+    cpu["L"] = [cpu["L"][0]] * 3
+    dev["L"] = [dev["L"][0]] * 3
+    _cmp_full(prob, cpu, H.run_prefill(prob, dev), what="shared LR cache")
+
+
+def test_bf16_split_invariance_and_determinism(monkeypatch):
+    prob = workloads.custom("bf16-split", "bf16", 8, 2, 128, (32,), [90], [3000], [0], seed=630)
+    cpu, dev = H.device_inputs(prob)
+    outs = {}
+    for target in ("1", "64", "4096"):
+        monkeypatch.setenv("LRA_PREFILL_TARGET_WG", target)
+        outs[target] = H.run_prefill(prob, dev).float().cpu().numpy()
+        again = H.run_prefill(prob, dev).float().cpu().numpy()
+        assert np.array_equal(outs[target], again), "repeat call not bitwise identical"
+    want = H.oracle_all(prob, cpu)
+    for k, v in outs.items():
+        H.assert_bf16_close(v, want, f"target {k}")
+    for k in ("64", "4096"):
+        assert np.abs(outs[k] - outs["1"]).max() <= 4e-3
+
+
+def test_bf16_empty_requests():
+    prob = workloads.custom("bf16-empty", "bf16", 8, 2, 128, (16,), [0, 20, 0], [10, 80, 0],
+                            [0, 0, 0], seed=640)
+    cpu, dev = H.device_inputs(prob)
+    O = torch.full_like(dev["Q"], 7.0)
+    H.run_prefill(prob, dev, O=O)
+    _cmp_full(prob, cpu, O)
+
+
+def test_bf16_decode_small_batch():
+    prob = workloads.custom("bf16-decode", "bf16", 32, 8, 128, (16, 64, 8), [1] * 6,
+                            [1, 63, 64, 65, 1000, 5000], [0, 1, 2, 0, 1, 2], seed=650)
+    cpu, dev = H.device_inputs(prob)
+    _cmp_full(prob, cpu, H.run_decode(prob, dev))
+    # prefill with one query per request is the same computation
+    _cmp_full(prob, cpu, H.run_prefill(prob, dev), what="decode via prefill")
+
+
+@pytest.mark.parametrize("chunk", ["64", "1024", "100000"])
+def test_bf16_decode_split_counts(chunk, monkeypatch):
+    monkeypatch.setenv("LRA_DECODE_CHUNK", chunk)
+    prob = workloads.custom("bf16-decode-split", "bf16", 16, 2, 64, (32,), [1, 1], [2000, 129],
+                            [0, 0], seed=660)
+    cpu, dev = H.device_inputs(prob)
+    _cmp_full(prob, cpu, H.run_decode(prob, dev))
+
+
+# ---------------------------------------------------------------------------------------
+# LR precompute
+# ---------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,T,dm,ranks", [("bf16", 300, 256, (8, 16, 64)),
+                                              ("bf16", 1000, 512, (64, 64, 64)),
+                                              ("bf16", 129, 4096, (32,)),
+                                              ("f32", 77, 136, (8, 24))])
+def test_precompute(dtype, T, dm, ranks):
+    import oracle
+    from shared_rank_kv_amd import inputs, lra
+    p = workloads.PrecomputeProblem("pre-small", dtype, T, dm, ranks, seed=700 + T)
+    X = p.X()
+    A = [p.A(a) for a in range(len(ranks))]
+    A_cat = torch.cat(A, dim=1).contiguous()
+    outs = [torch.full((T, r), float("nan"), dtype=X.dtype, device="cuda") for r in ranks]
+    lra.lra_precompute_lr(X.cuda(), A_cat.cuda(), ranks, outs)
+    torch.cuda.synchronize()
+    Xf = inputs.to_f64(X)
+    want = oracle.lr_precompute(Xf, [inputs.to_f64(a) for a in A])
+    for a in range(len(ranks)):
+        got = outs[a].double().cpu().numpy()
+        # fp32 accumulation bound plus (bf16) half an ulp of the rounded output
+        bound = dm * 2.0 ** -23 * (np.abs(Xf) @ np.abs(inputs.to_f64(A[a])))
+        if dtype == "bf16":
+            bound = bound + 2.0 ** -8 * np.abs(want[a])
+        assert np.all(np.abs(got - want[a]) <= bound + 1e-30), f"agent {a}"
+
+
+def test_precompute_into_column_blocks_of_one_buffer():
+    from shared_rank_kv_amd import lra
+    p = workloads.PrecomputeProblem("pre-cols", "bf16", 200, 256, (16, 32), seed=710)
+    X, A = p.X(), [p.A(0), p.A(1)]
+    A_cat = torch.cat(A, 1).contiguous().cuda()
+    buf = torch.zeros(200, 48, dtype=torch.bfloat16, device="cuda")
+    lra.lra_precompute_lr(X.cuda(), A_cat, (16, 32), [buf[:, :16], buf[:, 16:]])
+    sep = [torch.zeros(200, r, dtype=torch.bfloat16, device="cuda") for r in (16, 32)]
+    lra.lra_precompute_lr(X.cuda(), A_cat, (16, 32), sep)
+    torch.cuda.synchronize()
+    assert torch.equal(buf[:, :16], sep[0]) and torch.equal(buf[:, 16:], sep[1])
