@@ -1,0 +1,315 @@
+#!/usr/bin/env python3
+"""Benchmark of the Flash-LoRA-Attention hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--mixed] [--no-cpu-baseline]
+
+Headline (the JSON line's `value`): bf16 Flash-LoRA-Attention prefill throughput in
+TFLOP/s (algorithmic FLOP) on the Llama-3-8B-shaped single-layer workload: 1024 new causal
+queries after an 8192-token shared context (9216 keys), 32 q / 8 kv heads, head_dim 128,
+LoRA rank 16, agent 0 of 3.  A step is one lra_attn_prefill call on it; K steps are timed
+back to back between device synchronisations.
+
+Also reported, each timed on its own (HIP events around every call, the 256 MB MALL
+flushed between calls of the HBM-bound ones):
+  decode      64 requests x 16384 keys, one query each, rank 16, 4 agents  (HBM GB/s)
+  precompute  L = X·[A_1..A_3], X [32768, 4096], ranks 3 x 64              (HBM GB/s)
+  longctx     512 queries over 32768 keys, rank 64, L from the precompute   (TFLOP/s)
+  mixed       (--mixed) 32 layers of a 32-request batch, ranks 8/16/32/64   (roofline time)
+and the CPU fp64 oracle timed on a bounded sample of the headline workload.
+
+Prints ONE JSON line on stdout.  Inputs are seeded synthetic tensors resident in HBM
+before timing starts.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Flash-LoRA-Attn prefill TFLOP/s + decode HBM GB/s (% of MI355X roofline)"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _events(n):
+    import torch
+    return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+
+class Flusher:
+    """Evicts the 256 MB Infinity Cache (MALL) by writing a 512 MB buffer."""
+
+    def __init__(self):
+        import torch
+        self.buf = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+
+    def __call__(self):
+        self.buf.fill_(1)
+
+
+def time_calls(fn, steps, warmup, flush=None):
+    """Per-call durations (ms, HIP events on the current stream) and the total time of the
+    K calls issued back to back (ms; only when no flush is interleaved)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    st, en = _events(steps), _events(steps)
+    t0, t1 = _events(2)
+    t0.record()
+    for i in range(steps):
+        if flush is not None:
+            flush()
+        st[i].record()
+        fn()
+        en[i].record()
+    t1.record()
+    torch.cuda.synchronize()
+    per = np.array([s.elapsed_time(e) for s, e in zip(st, en)])
+    total = t0.elapsed_time(t1)
+    return per, total
+
+
+def roof(achieved, peak, unit, bound, traffic=None):
+    return {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": traffic}
+
+
+def upload(prob, L=None):
+    cpu = {"Q": prob.Q(), "K": prob.K(), "V": prob.V()}
+    dev = {k: v.cuda() for k, v in cpu.items()}
+    dev["L"] = L if L is not None else [prob.L(a).cuda() if prob.ranks[a] else None
+                                        for a in range(prob.n_agents)]
+    dev["B"] = [prob.B(a).cuda() if prob.ranks[a] else None for a in range(prob.n_agents)]
+    return cpu, dev
+
+
+def prefill_call(prob, dev, ws):
+    from shared_rank_kv_amd import lra
+    O = torch_empty_like(dev["Q"])
+
+    def fn():
+        lra.lra_attn_prefill(dev["Q"], dev["K"], dev["V"], dev["L"], dev["B"], prob.q_start,
+                             prob.q_len, prob.k_start, prob.k_len, prob.agent_idx, O=O,
+                             workspace=ws)
+    return fn
+
+
+def torch_empty_like(t):
+    import torch
+    return torch.empty_like(t)
+
+
+def workspace_for(prob, decode):
+    import torch
+    from shared_rank_kv_amd import lra
+    n = lra.lra_attn_workspace_bytes(torch.bfloat16 if prob.dtype == "bf16" else torch.float32,
+                                     decode, None if decode else prob.q_len, prob.k_len,
+                                     prob.n_q_heads, prob.n_kv_heads, prob.head_dim,
+                                     max(prob.ranks))
+    return torch.empty(max(n, 1), dtype=torch.uint8, device="cuda") if n else None
+
+
+def bench_llama_prefill(steps, warmup):
+    from shared_rank_kv_amd import accounting, workloads
+    prob = workloads.llama_prefill(agents=(0,))
+    cpu, dev = upload(prob)
+    ws = workspace_for(prob, False)
+    fn = prefill_call(prob, dev, ws)
+    per, total = time_calls(fn, steps, warmup)
+    flop, nbytes = accounting.attention_work(prob)
+    return prob, cpu, dev, {"flop": flop, "bytes": nbytes, "per_ms": per, "total_ms": total}
+
+
+def bench_decode(steps, warmup, flush):
+    from shared_rank_kv_amd import accounting, lra, workloads
+    prob = workloads.decode_batch()
+    t = time.time()
+    cpu, dev = upload(prob)
+    log(f"[bench] decode inputs ready in {time.time() - t:.1f}s")
+    ws = workspace_for(prob, True)
+    O = torch_empty_like(dev["Q"])
+
+    def fn():
+        lra.lra_attn_decode(dev["Q"], dev["K"], dev["V"], dev["L"], dev["B"], prob.k_start,
+                            prob.k_len, prob.agent_idx, O=O, workspace=ws)
+    per, _ = time_calls(fn, steps, warmup, flush)
+    flop, nbytes = accounting.attention_work(prob)
+    del dev, cpu
+    ms = float(np.median(per))
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": prob.name, "value": round(gbs, 1), "unit": "GB/s",
+            "ms_per_call": round(ms, 4), "bytes": nbytes, "flop": flop,
+            "roofline": roof(gbs, accounting.PEAK_HBM_GBS, "GB/s", "hbm")}
+
+
+def bench_longctx(steps, warmup, flush):
+    import torch
+    from shared_rank_kv_amd import accounting, lra, workloads
+    pre = workloads.longctx_precompute()
+    X = pre.X().cuda()
+    A_cat = torch.cat([pre.A(a) for a in range(3)], 1).contiguous().cuda()
+    Ls = [torch.empty(pre.T, r, dtype=torch.bfloat16, device="cuda") for r in pre.ranks]
+
+    def pfn():
+        lra.lra_precompute_lr(X, A_cat, pre.ranks, Ls)
+    per, _ = time_calls(pfn, steps, warmup, flush)
+    pflop, pbytes = accounting.precompute_work(pre)
+    pms = float(np.median(per))
+    pgbs = pbytes / (pms * 1e-3) / 1e9
+    precompute = {"workload": pre.name, "value": round(pgbs, 1), "unit": "GB/s",
+                  "tflops": round(pflop / (pms * 1e-3) / 1e12, 1), "ms_per_call": round(pms, 4),
+                  "bytes": pbytes, "flop": pflop,
+                  "roofline": roof(pgbs, accounting.PEAK_HBM_GBS, "GB/s", "hbm")}
+    del X
+    prob = workloads.longctx_prefill(agents=(0,))
+    _, dev = upload(prob, L=Ls)
+    ws = workspace_for(prob, False)
+    per, _ = time_calls(prefill_call(prob, dev, ws), steps, warmup)
+    flop, nbytes = accounting.attention_work(prob)
+    ms = float(np.median(per))
+    tf = flop / (ms * 1e-3) / 1e12
+    longctx = {"workload": prob.name, "value": round(tf, 1), "unit": "TFLOP/s",
+               "ms_per_call": round(ms, 4), "flop": flop, "bytes": nbytes,
+               "roofline": roof(tf, accounting.PEAK_BF16_TFLOPS, "TFLOP/s", "mfma")}
+    return precompute, longctx
+
+
+def bench_mixed(steps, warmup):
+    import torch
+    from shared_rank_kv_amd import accounting, lra, workloads
+    layers = []
+    t = time.time()
+    tflop = tbytes = 0
+    for layer in range(workloads.MIXED_LAYERS):
+        prob = workloads.mixed_batch_layer(layer)
+        _, dev = upload(prob)
+        dev["ws"] = workspace_for(prob, False)
+        dev["O"] = torch.empty_like(dev["Q"])
+        f, b = accounting.attention_work(prob)
+        tflop += f
+        tbytes += b
+        layers.append((prob, dev))
+    log(f"[bench] mixed-batch inputs (32 layers) ready in {time.time() - t:.1f}s")
+
+    def fn():
+        for prob, dev in layers:
+            lra.lra_attn_prefill(dev["Q"], dev["K"], dev["V"], dev["L"], dev["B"], prob.q_start,
+                                 prob.q_len, prob.k_start, prob.k_len, prob.agent_idx,
+                                 O=dev["O"], workspace=dev["ws"])
+    per, _ = time_calls(fn, max(3, steps // 4), max(1, warmup // 2))
+    ms = float(np.median(per))
+    ideal_ms = max(tflop / (accounting.PEAK_BF16_TFLOPS * 1e12),
+                   tbytes / (accounting.PEAK_HBM_GBS * 1e9)) * 1e3
+    del layers
+    torch.cuda.empty_cache()
+    return {"workload": "mixed32-32req-ranks8-16-32-64", "ms_per_32_layers": round(ms, 3),
+            "flop": tflop, "bytes": tbytes, "tflops": round(tflop / (ms * 1e-3) / 1e12, 1),
+            "roofline_ms": round(ideal_ms, 3), "frac_of_roofline": round(ideal_ms / ms, 4)}
+
+
+def cpu_baseline(prob, cpu, target_s=10.0):
+    """The fp64 oracle on the first n query rows (all heads) of the headline workload,
+    n chosen for ~target_s seconds of host time; reported in the headline's unit."""
+    import oracle
+    from shared_rank_kv_amd import accounting, inputs
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        cores = os.cpu_count()
+    lk, lq = int(prob.k_len[0]), int(prob.q_len[0])
+    Q = inputs.to_f64(cpu["Q"][:lq])
+    K = inputs.to_f64(cpu["K"])
+    V = inputs.to_f64(cpu["V"])
+    L = inputs.to_f64(prob.L(0))
+    B = inputs.to_f64(prob.B(0))
+
+    def run(n):
+        rows = np.arange(n)
+        t = time.perf_counter()
+        oracle.attention_request(Q[rows], K, V, L, B, positions=(lk - lq) + rows)
+        return time.perf_counter() - t
+
+    n0 = 32
+    t0 = run(n0)
+    n = int(min(lq, max(n0, n0 * target_s / max(t0, 1e-3))))
+    t = run(n)
+    r = prob.ranks[0]
+    D, Hq = prob.head_dim, prob.n_q_heads
+    pairs = sum(lk - lq + i + 1 for i in range(n))
+    flop = Hq * pairs * (4 * D + 2 * r) + Hq * n * 2 * r * D
+    return {"value": round(flop / t / 1e12, 5), "unit": "TFLOP/s", "cores": cores,
+            "kind": "oracle", "seconds": round(t, 2),
+            "sample": f"{prob.name}, agent 0, query rows 0..{n - 1} of {lq}, all {Hq} q heads, "
+                      f"fp64 numpy/BLAS on {platform.processor() or platform.machine()}"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--mixed", action="store_true", help="also time the 32-layer mixed batch")
+    ap.add_argument("--only-prefill", action="store_true", help="headline workload only")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    from shared_rank_kv_amd import accounting
+
+    log("[bench] llama prefill (headline)")
+    prob, cpu, dev, r = bench_llama_prefill(args.steps, args.warmup)
+    ms_step = r["total_ms"] / args.steps
+    value = r["flop"] / (ms_step * 1e-3) / 1e12
+    kern_ms = float(np.mean(r["per_ms"]))
+    achieved = r["flop"] / (kern_ms * 1e-3) / 1e12
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: seeded Gaussian Llama-3-8B-shaped base K/V, LR caches and B",
+        "config": {"workload": prob.name, "q_len": 1024, "k_len": 9216, "q_heads": 32,
+                   "kv_heads": 8, "head_dim": 128, "rank": 16, "agents": 3, "timed_agent": 0,
+                   "flop_per_step": r["flop"], "bytes_per_step": r["bytes"]},
+        "roofline": roof(achieved, accounting.PEAK_BF16_TFLOPS, "TFLOP/s", "mfma"),
+        "roofline_kernel": "lra_attn_prefill call (attention kernel, plus the combine pass "
+                           "when the planner splits keys)",
+    }
+    del dev
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        out["cpu_baseline"] = cpu_baseline(prob, cpu)
+    if not args.only_prefill:
+        flush = Flusher()
+        log("[bench] decode")
+        out["decode"] = bench_decode(args.steps, args.warmup, flush)
+        log("[bench] precompute + long-context prefill")
+        out["precompute"], out["longctx_prefill"] = bench_longctx(args.steps, args.warmup, flush)
+        del flush
+        torch.cuda.empty_cache()
+        if args.mixed:
+            log("[bench] mixed 32-layer batch")
+            out["mixed"] = bench_mixed(args.steps, args.warmup)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

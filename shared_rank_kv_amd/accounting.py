@@ -1,0 +1,63 @@
+"""Algorithmic work of the hot path, for roofline reporting.
+
+Counting rules (algorithmic work only):
+* attention FLOP = sum over q heads and unmasked (query, key) pairs of 4*D + 2*r
+  (Q·Kᵀ, P·V_base and P·L, 2 FLOP per multiply-add) plus 2*r*D per query row and q head
+  for the up-projection (P·L)·B; softmax work, padding (rank to 32-wide MFMA blocks,
+  unused rows of a tile) and the full-width expansion the method avoids are not counted;
+* attention bytes = K_base and V_base rows once (rows shared by several requests count
+  once), each request's selected LR-cache rows, B once per agent used, Q and O;
+* precompute FLOP = 2*T*d_model*sum(r); bytes = X + A_cat + the L outputs.
+The split-key workspace traffic is implementation overhead and is not counted.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+PEAK_FP32_TFLOPS = 157.3
+
+
+def _elem(dtype):
+    return 2 if dtype == "bf16" else 4
+
+
+def attention_work(prob):
+    """(flop, bytes) of one lra_attn_prefill / lra_attn_decode call on ``prob``."""
+    e = _elem(prob.dtype)
+    D, Hq, Hkv = prob.head_dim, prob.n_q_heads, prob.n_kv_heads
+    flop = 0
+    l_bytes = 0
+    agents = set()
+    spans = []
+    for b in range(prob.batch):
+        lq, lk = int(prob.q_len[b]), int(prob.k_len[b])
+        if lq == 0:
+            continue
+        r = prob.ranks[int(prob.agent_idx[b])]
+        pairs = lq * (lk - lq) + lq * (lq + 1) // 2
+        flop += Hq * pairs * (4 * D + 2 * r) + Hq * lq * 2 * r * D
+        l_bytes += lk * r * e
+        if r:
+            agents.add(int(prob.agent_idx[b]))
+        spans.append((int(prob.k_start[b]), int(prob.k_start[b]) + lk))
+    # unique key rows
+    rows = 0
+    end = -1
+    for s, t in sorted(spans):
+        if t > end:
+            rows += t - max(s, end)
+            end = t
+    kv_bytes = rows * Hkv * D * e * 2
+    b_bytes = sum(prob.ranks[a] * Hkv * D * e for a in agents)
+    qo_bytes = int(np.sum(prob.q_len)) * Hq * D * e * 2
+    return flop, kv_bytes + l_bytes + b_bytes + qo_bytes
+
+
+def precompute_work(p):
+    e = _elem(p.dtype)
+    R = sum(p.ranks)
+    flop = 2 * p.T * p.d_model * R
+    return flop, (p.T * p.d_model + p.d_model * R + p.T * R) * e
