@@ -256,13 +256,32 @@ def cpu_baseline(prob, cpu, target_s=10.0):
                       f"fp64 numpy/BLAS on {platform.processor() or platform.machine()}"}
 
 
+def run_only(args):
+    if args.only == "copy":
+        import torch
+        src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        per, _ = time_calls(lambda: dst.copy_(src), args.steps, args.warmup)
+        ms = float(np.median(per))
+        return {"workload": "device copy 1 GiB", "ms": ms, "GB/s": 2 * (1 << 30) / ms / 1e6,
+                "read_bytes": 1 << 30, "write_bytes": 1 << 30}
+    if args.only == "decode":
+        return bench_decode(args.steps, args.warmup, Flusher())
+    if args.only == "longctx":
+        pre, lc = bench_longctx(args.steps, args.warmup, Flusher())
+        return {"precompute": pre, "longctx_prefill": lc}
+    return bench_mixed(args.steps, args.warmup)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--mixed", action="store_true", help="also time the 32-layer mixed batch")
-    ap.add_argument("--only-prefill", action="store_true", help="headline workload only")
+    ap.add_argument("--only", choices=["prefill", "decode", "longctx", "mixed", "copy"],
+                    help="time one workload only (for profiling); prints its JSON object. "
+                         "'copy' times a 1 GiB device copy, the reference for HBM counters")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -274,6 +293,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     from shared_rank_kv_amd import accounting
+    if args.only and args.only != "prefill":
+        print(json.dumps(run_only(args)), flush=True)
+        return
 
     log("[bench] llama prefill (headline)")
     prob, cpu, dev, r = bench_llama_prefill(args.steps, args.warmup)
@@ -297,7 +319,7 @@ def main():
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline(prob, cpu)
-    if not args.only_prefill:
+    if not args.only:
         flush = Flusher()
         log("[bench] decode")
         out["decode"] = bench_decode(args.steps, args.warmup, flush)

@@ -66,67 +66,55 @@ __device__ __forceinline__ bf16x8 join(i16x4 lo, i16x4 hi) {
 
 __device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// 64 rows x D bf16 from a strided source into LDS (row = D*2 bytes, 16-byte chunk c of
-// row k stored at position c ^ (k % (D/8))).  Rows at or past `valid` repeat row valid-1
-// so the tile holds only finite data; the caller masks them.
+__device__ __forceinline__ float lane_bcast(float x, int src) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), src));
+}
+
+// LDS layouts of the 64-key tiles (rows are D*2 bytes; 16-byte chunk c of row k lives at
+// position c ^ swz(k)).  K is read by 32 consecutive rows at one chunk (ds_read_b128), V by
+// ds_read_b64_tr_b16 over 4 consecutive rows x 4 consecutive chunks per half-wave; each
+// swizzle makes its own read pattern bank-conflict free on the 64 x 4-byte LDS banks.
 template <int D>
+__device__ __forceinline__ int swz_k(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
+template <int D>
+__device__ __forceinline__ int swz_v(int row) { return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1); }
+
+// 64 rows x D bf16 from a strided source into LDS with direct global->LDS loads.  Rows at
+// or past `valid` repeat row valid-1 so the tile holds only finite data (the caller masks
+// them out).  Each wave writes 1 KB units u = wave, wave+4, ...
+template <int D, bool VSWZ>
 __device__ __forceinline__ void load_rows(const bf16* src, int64_t stride, int r0, int valid,
                                           LDS char* dst, int wave, int lane) {
   constexpr int CPR = D / 8;
   constexpr int RPU = 64 / CPR;        // rows per 1 KB unit
   constexpr int UNITS = 64 / RPU;
 #pragma unroll
-  for (int u = wave; u < UNITS; u += 4) {
+  for (int i = 0; i < UNITS / 4; ++i) {
+    const int u = wave + 4 * i;
     const int row = u * RPU + lane / CPR;
-    const int c = (lane % CPR) ^ (row % CPR);
+    const int c = (lane % CPR) ^ (VSWZ ? swz_v<D>(row) : swz_k<D>(row));
     const int key = min(r0 + row, valid - 1);
     __builtin_amdgcn_global_load_lds((const void*)(src + (int64_t)key * stride + c * 8),
                                      (LDS void*)(dst + u * 1024), 16, 0, 0);
   }
 }
 
-// 64 rows x rank bf16 of an LR cache, rows packed densely (rank*2 bytes) in LDS.
+// 64 rows x rank bf16 of an LR cache into an LDS tile of 64 x 64 bf16 (128-byte rows; the
+// 64-byte halves of rows with bit 1 set are swapped against bank conflicts).  Chunks past
+// the rank are not loaded: the tile is zeroed once, so those columns read as 0.
 __device__ __forceinline__ void load_lr(const bf16* src, int64_t ldl, int rank, int r0, int valid,
                                         LDS char* dst, int wave, int lane) {
-  const int row_bytes = rank * 2;
-  const int units = rank / 8;
-  for (int u = wave; u < units; u += 4) {
-    const int off = u * 1024 + lane * 16;
-    const int row = off / row_bytes;
-    const int c = (off - row * row_bytes) >> 4;
-    const int key = min(r0 + row, valid - 1);
-    __builtin_amdgcn_global_load_lds((const void*)(src + (int64_t)key * ldl + c * 8),
-                                     (LDS void*)(dst + u * 1024), 16, 0, 0);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int u = wave + 4 * i;
+    const int row = u * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ (((row >> 1) & 1) * 4);
+    if (c * 8 < rank) {
+      const int key = min(r0 + row, valid - 1);
+      __builtin_amdgcn_global_load_lds((const void*)(src + (int64_t)key * ldl + c * 8),
+                                       (LDS void*)(dst + u * 1024), 16, 0, 0);
+    }
   }
-}
-
-// A operand (rows = D lanes of block db, k = 16 keys of step st) of Oᵀ += Vᵀ·Pᵀ from a
-// swizzled 64 x D tile.  Key order within the step matches pfrag().
-template <int D>
-__device__ __forceinline__ bf16x8 vfrag(const LDS char* tile, int st, int db, int lane) {
-  constexpr int CPR = D / 8;
-  const int g16 = lane >> 4, jj = lane & 15;
-  const int key = (st >> 1) * 32 + (st & 1) * 16 + (g16 >> 1) * 4 + (jj >> 2);
-  const int d = db * 32 + (g16 & 1) * 16 + (jj & 3) * 4;
-  const int c = d >> 3, sub = (d & 7) * 2;
-  const int k1 = key + 8;
-  i16x4 lo = tr_read(tile + key * (D * 2) + ((c ^ (key % CPR)) << 4) + sub);
-  i16x4 hi = tr_read(tile + k1 * (D * 2) + ((c ^ (k1 % CPR)) << 4) + sub);
-  return join(lo, hi);
-}
-
-// A operand of (P·L)ᵀ += Lᵀ·Pᵀ: rows = rank lanes rb*32.., zero for rows >= rank.
-__device__ __forceinline__ bf16x8 lfrag(const LDS char* tile, int rank, int st, int rb, int lane) {
-  const int g16 = lane >> 4, jj = lane & 15;
-  const int key = (st >> 1) * 32 + (st & 1) * 16 + (g16 >> 1) * 4 + (jj >> 2);
-  int rho = rb * 32 + (g16 & 1) * 16 + (jj & 3) * 4;
-  if (rho >= rank) rho = 0;                               // keep the read in bounds
-  i16x4 lo = tr_read(tile + key * (rank * 2) + rho * 2);
-  i16x4 hi = tr_read(tile + (key + 8) * (rank * 2) + rho * 2);
-  bf16x8 v = join(lo, hi);
-  const int my_rho = rb * 32 + (lane & 31);
-  if (my_rho >= rank) v = bf16x8{};
-  return v;
 }
 
 // B operand for key step st (16 keys) from the transposed score/probability block.
@@ -137,14 +125,58 @@ __device__ __forceinline__ bf16x8 pfrag(const f32x16& s, int half) {
   return r;
 }
 
+// Per-lane LDS byte offsets of the MFMA operands, fixed for the whole key loop.
 template <int D>
+struct Offsets {
+  static constexpr int KS = D / 16, DB = D / 32;
+  int k[KS];     // K rows (A of Sᵀ=K·Qᵀ): + kb2 * 32 * D*2
+  int v[DB];     // V tr reads (A of Oᵀ+=Vᵀ·Pᵀ): + key base * D*2
+  int l[2];      // LR tr reads (A of (P·L)ᵀ+=Lᵀ·Pᵀ): + key base * 128
+  __device__ __forceinline__ Offsets(int lane) {
+    const int col = lane & 31, hi = lane >> 5, g16 = lane >> 4, jj = lane & 15;
+    const int sk = swz_k<D>(col);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) k[ks] = col * (D * 2) + (((2 * ks + hi) ^ sk) << 4);
+    const int e = jj >> 2;                       // key within the 4-row group
+    const int krow = hi * 4 + e;                 // + multiple of 8 (immediate)
+    const int cl = (g16 & 1) * 2 + ((jj & 3) >> 1);
+    const int sub = (jj & 1) * 8;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      v[db] = krow * (D * 2) + (((db * 4 + cl) ^ swz_v<D>(krow)) << 4) + sub;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const int rho = rb * 32 + (g16 & 1) * 16 + (jj & 3) * 4;
+      l[rb] = krow * 128 + ((rho * 2) ^ (((krow >> 1) & 1) * 64));
+    }
+  }
+};
+
+template <int D>
+__device__ __forceinline__ bf16x8 vfrag(const LDS char* tile, int off, int key0) {
+  i16x4 lo = tr_read(tile + off + key0 * (D * 2));
+  i16x4 hi = tr_read(tile + off + (key0 + 8) * (D * 2));
+  return join(lo, hi);
+}
+
+__device__ __forceinline__ bf16x8 lfrag(const LDS char* tile, int off, int key0) {
+  i16x4 lo = tr_read(tile + off + key0 * 128);
+  i16x4 hi = tr_read(tile + off + (key0 + 8) * 128);
+  return join(lo, hi);
+}
+
+// Threshold (log2 units) by which a row max may exceed the running max before the
+// accumulators are rescaled; probabilities then stay below 2^8, which fp32 and bf16 hold
+// exactly as well as values below 1.
+constexpr float kRescaleSlack = 8.0f;
+
+template <int D, int RB>
 __global__ __launch_bounds__(256, 2) void fla_attn_bf16(const AttnArgs args) {
   const AttnArgs* A = (const AttnArgs*)__builtin_amdgcn_kernarg_segment_ptr();
   constexpr int DB = D / 32;           // 32-row blocks of the transposed output
   constexpr int KS = D / 16;           // k-steps of the score product
-  constexpr int CPR = D / 8;
   constexpr int TILE_KV = 64 * D * 2;  // bytes of one K or V tile
-  constexpr int TILE_L = 64 * 64 * 2;  // bytes of one LR tile (max rank)
+  constexpr int TILE_L = 64 * 64 * 2;  // bytes of one LR tile (64 x 64 bf16)
   constexpr int BUF = 2 * TILE_KV + TILE_L;
   __shared__ __attribute__((aligned(1024))) char smem_raw[2 * BUF];
   LDS char* smem = (LDS char*)smem_raw;
@@ -189,11 +221,13 @@ __global__ __launch_bounds__(256, 2) void fla_attn_bf16(const AttnArgs args) {
   const int ke = min(min(Lk, kb + tps * kTileKeys), kend_causal);
   const int n_tiles = ke > kb ? (ke - kb + kTileKeys - 1) / kTileKeys : 0;
   const int mask_from = min(kmask_from, ke);
+  // last visible key of this lane's row inside the range, minus its key-lane offset
+  const int vis_last = min(pos, ke - 1) - hi * 4;
 
   const int64_t kv_stride = (int64_t)Hkv * D;
   const bf16* Kg = (const bf16*)A->K + ((int64_t)k_start * Hkv + g) * D;
   const bf16* Vg = (const bf16*)A->V + ((int64_t)k_start * Hkv + g) * D;
-  const bf16* Lg = rank ? (const bf16*)AG.L + (int64_t)k_start * AG.ldl : nullptr;
+  const bf16* Lg = RB ? (const bf16*)AG.L + (int64_t)k_start * AG.ldl : nullptr;
 
   // ---- Q fragments (B operand of Sᵀ = K·Qᵀ): lane holds Q[row col][ks*16 + hi*8 .. +7]
   bf16x8 qf[KS];
@@ -203,81 +237,94 @@ __global__ __launch_bounds__(256, 2) void fla_attn_bf16(const AttnArgs args) {
     for (int ks = 0; ks < KS; ++ks)
       qf[ks] = valid ? *(const bf16x8*)(qrow + ks * 16 + hi * 8) : bf16x8{};
   }
+  const Offsets<D> off(lane);
 
   f32x16 accV[DB];
-  f32x16 accL[2];
+  f32x16 accL[RB > 0 ? RB : 1];
 #pragma unroll
   for (int i = 0; i < DB; ++i) accV[i] = f32x16{};
-  accL[0] = accL[1] = f32x16{};
+#pragma unroll
+  for (int i = 0; i < (RB > 0 ? RB : 1); ++i) accL[i] = f32x16{};
   float m_run = kNegBig, l_run = 0.f;
   const float sl2 = A->scale_log2;
-  const int RB = rank > 32 ? 2 : (rank > 0 ? 1 : 0);
 
+  if (RB) {
+    // LR tiles: columns past the rank are never loaded and must read as zero
+    const f32x4 z = {};
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      *(LDS f32x4*)(smem + 2 * TILE_KV + tid * 32 + i * 16) = z;
+      *(LDS f32x4*)(smem + BUF + 2 * TILE_KV + tid * 32 + i * 16) = z;
+    }
+    __syncthreads();
+  }
   if (n_tiles > 0) {
-    load_rows<D>(Kg, kv_stride, kb, ke, smem, wave, lane);
-    load_rows<D>(Vg, kv_stride, kb, ke, smem + TILE_KV, wave, lane);
-    if (rank) load_lr(Lg, AG.ldl, rank, kb, ke, smem + 2 * TILE_KV, wave, lane);
+    load_rows<D, false>(Kg, kv_stride, kb, ke, smem, wave, lane);
+    load_rows<D, true>(Vg, kv_stride, kb, ke, smem + TILE_KV, wave, lane);
+    if (RB) load_lr(Lg, AG.ldl, rank, kb, ke, smem + 2 * TILE_KV, wave, lane);
   }
   wait_loads();
   __syncthreads();
 
   for (int j = 0; j < n_tiles; ++j) {
     const int k0 = kb + j * kTileKeys;
-    LDS char* cur = smem + (j & 1) * BUF;
+    const LDS char* cur = smem + (j & 1) * BUF;
     if (j + 1 < n_tiles) {
       LDS char* nxt = smem + ((j + 1) & 1) * BUF;
-      load_rows<D>(Kg, kv_stride, k0 + kTileKeys, ke, nxt, wave, lane);
-      load_rows<D>(Vg, kv_stride, k0 + kTileKeys, ke, nxt + TILE_KV, wave, lane);
-      if (rank) load_lr(Lg, AG.ldl, rank, k0 + kTileKeys, ke, nxt + 2 * TILE_KV, wave, lane);
+      load_rows<D, false>(Kg, kv_stride, k0 + kTileKeys, ke, nxt, wave, lane);
+      load_rows<D, true>(Vg, kv_stride, k0 + kTileKeys, ke, nxt + TILE_KV, wave, lane);
+      if (RB) load_lr(Lg, AG.ldl, rank, k0 + kTileKeys, ke, nxt + 2 * TILE_KV, wave, lane);
     }
     if (wave_active) {
       // -- Sᵀ = K·Qᵀ for 64 keys (two 32-key blocks)
       f32x16 s[2];
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
-        s[kb2] = f32x16{};
-        const int krow = kb2 * 32 + col;
-        const LDS char* rowp = cur + krow * (D * 2);
+        bf16x8 kf[KS];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const int c = ks * 2 + hi;
-          bf16x8 kf = *(const LDS bf16x8*)(rowp + ((c ^ (krow % CPR)) << 4));
-          s[kb2] = mfma32(kf, qf[ks], s[kb2]);
-        }
+        for (int ks = 0; ks < KS; ++ks)
+          kf[ks] = *(const LDS bf16x8*)(cur + off.k[ks] + kb2 * 32 * (D * 2));
+        s[kb2] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) s[kb2] = mfma32(kf[ks], qf[ks], s[kb2]);
       }
-      // -- scale, causal mask, online softmax (one running max/sum per query row)
-      const bool need_mask = k0 + kTileKeys > mask_from;
+      // -- causal mask (only tiles that reach past the first row's last key)
+      if (k0 + kTileKeys > mask_from) {
+        const int lim = vis_last - k0;
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            if (kb2 * 32 + (e >> 2) * 8 + (e & 3) > lim) s[kb2][e] = -INFINITY;
+      }
+      // -- online softmax; the running max moves only when a row max outgrows it by more
+      // than kRescaleSlack, so most tiles skip the accumulator rescale
       float mx = -INFINITY;
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          float v = s[kb2][e] * sl2;
-          if (need_mask) {
-            const int key = k0 + kb2 * 32 + (e >> 2) * 8 + hi * 4 + (e & 3);
-            if (key > pos || key >= ke) v = -INFINITY;
-          }
-          s[kb2][e] = v;
-          mx = fmaxf(mx, v);
-        }
-      mx = half_max(mx);
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
+        for (int e = 0; e < 16; e += 2) mx = fmaxf(mx, fmaxf(s[kb2][e], s[kb2][e + 1]));
+      mx = half_max(mx) * sl2;
+      if (__any(mx > m_run + kRescaleSlack)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int i = 0; i < DB; ++i) accV[i] *= alpha;
+#pragma unroll
+        for (int i = 0; i < RB; ++i) accL[i] *= alpha;
+      }
       float psum = 0.f;
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const float p = __builtin_amdgcn_exp2f(s[kb2][e] - m_new);
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[kb2][e], sl2, -m_run));
           s[kb2][e] = p;
           psum += p;
         }
-      l_run = l_run * alpha + psum;
-#pragma unroll
-      for (int i = 0; i < DB; ++i) accV[i] *= alpha;
-      accL[0] *= alpha;
-      accL[1] *= alpha;
+      l_run += psum;
 
       // -- Oᵀ += V_baseᵀ·Pᵀ and (P·L)ᵀ += Lᵀ·Pᵀ with the same P
       const LDS char* vt = cur + TILE_KV;
@@ -285,10 +332,11 @@ __global__ __launch_bounds__(256, 2) void fla_attn_bf16(const AttnArgs args) {
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
         const bf16x8 pf = pfrag(s[st >> 1], st & 1);
+        const int key0 = (st >> 1) * 32 + (st & 1) * 16;
 #pragma unroll
-        for (int db = 0; db < DB; ++db) accV[db] = mfma32(vfrag<D>(vt, st, db, lane), pf, accV[db]);
-        if (RB > 0) accL[0] = mfma32(lfrag(lt, rank, st, 0, lane), pf, accL[0]);
-        if (RB > 1) accL[1] = mfma32(lfrag(lt, rank, st, 1, lane), pf, accL[1]);
+        for (int db = 0; db < DB; ++db) accV[db] = mfma32(vfrag<D>(vt, off.v[db], key0), pf, accV[db]);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) accL[rb] = mfma32(lfrag(lt, off.l[rb], key0), pf, accL[rb]);
       }
     }
     wait_loads();
@@ -301,19 +349,20 @@ __global__ __launch_bounds__(256, 2) void fla_attn_bf16(const AttnArgs args) {
     const float inv = 1.f / l_tot;
 #pragma unroll
     for (int i = 0; i < DB; ++i) accV[i] *= inv;
-    if (rank) {
+    if (RB && rank > 0) {   // a rank-0 agent has no B (its pointer may be null)
       // B_g = B[:, g*D : (g+1)*D] is a "value tile" whose rows are the rank index.
-      load_rows<D>((const bf16*)AG.B + g * D, kv_stride, 0, rank, smem + TILE_KV, wave, lane);
+      load_rows<D, true>((const bf16*)AG.B + g * D, kv_stride, 0, rank, smem + TILE_KV, wave, lane);
       wait_loads();
       __syncthreads();
       if (wave_active) {
         const int nst = (rank + 15) / 16;
         for (int st = 0; st < nst; ++st) {
-          const f32x16 lsc = accL[st >> 1] * inv;
+          const f32x16 lsc = accL[(RB > 1) ? (st >> 1) : 0] * inv;
           const bf16x8 pf = pfrag(lsc, st & 1);
+          const int key0 = (st >> 1) * 32 + (st & 1) * 16;
 #pragma unroll
           for (int db = 0; db < DB; ++db)
-            accV[db] = mfma32(vfrag<D>(smem + TILE_KV, st, db, lane), pf, accV[db]);
+            accV[db] = mfma32(vfrag<D>(smem + TILE_KV, off.v[db], key0), pf, accV[db]);
         }
       }
     }
@@ -345,7 +394,8 @@ __global__ __launch_bounds__(256, 2) void fla_attn_bf16(const AttnArgs args) {
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        f32x4 v = {accL[rb][i * 4], accL[rb][i * 4 + 1], accL[rb][i * 4 + 2], accL[rb][i * 4 + 3]};
+        f32x4 v = {};
+        if (rb < RB) v = f32x4{accL[rb][i * 4], accL[rb][i * 4 + 1], accL[rb][i * 4 + 2], accL[rb][i * 4 + 3]};
         *(f32x4*)(pl + rb * 32 + i * 8 + hi * 4) = v;
       }
     if (hi == 0) {
@@ -355,25 +405,17 @@ __global__ __launch_bounds__(256, 2) void fla_attn_bf16(const AttnArgs args) {
   }
 }
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
-}
-
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  return x;
-}
-
 // Merge the key-split partial states of one output row (one wave per row):
 //   M = max m_s, w_s = 2^(m_s - M),
 //   O = (Σ w_s·(P·V_base)_s + (Σ w_s·(P·L)_s)·B_g) / Σ w_s·l_s
-// B is linear, so applying it once after the merge equals applying it per split.
+// B is linear, so applying it once after the merge equals applying it per split.  A lane
+// owns D/64 consecutive output lanes; split weights and the merged LR row are broadcast
+// with readlane.
 template <int D>
 __global__ __launch_bounds__(256) void fla_combine_bf16(const AttnArgs args) {
   const AttnArgs* A = (const AttnArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+  constexpr int DPL = D / 64;
+  typedef float fvec __attribute__((ext_vector_type(DPL)));
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + wave;
   if (row >= A->n_comb) return;
@@ -387,48 +429,61 @@ __global__ __launch_bounds__(256) void fla_combine_bf16(const AttnArgs args) {
   const int S = R.n_split;
   const AgentDesc& AG = A->agents[R.agent];
   const int rank = AG.rank;
-  auto prow = [&](int s) { return (int64_t)R.part_base + ((int64_t)s * R.q_len + t) * Hq + h; };
+  const int64_t p0 = (int64_t)R.part_base + (int64_t)t * Hq + h;   // split s adds s*Lq*Hq
+  const int64_t pstride = (int64_t)R.q_len * Hq;
 
   float m_s = kNegBig, l_s = 0.f;
   if (lane < S) {
-    m_s = A->ws_ml[prow(lane) * 2];
-    l_s = A->ws_ml[prow(lane) * 2 + 1];
+    const float2 ml = *(const float2*)(A->ws_ml + (p0 + lane * pstride) * 2);
+    m_s = ml.x;
+    l_s = ml.y;
   }
-  const float M = wave_max(m_s);
-  const float w_s = lane < S ? __builtin_amdgcn_exp2f(m_s - M) : 0.f;
-  const float l = wave_sum(w_s * l_s);
-
-  constexpr int DPL = D / 64;
-  float o[DPL];
+  float M = m_s;
 #pragma unroll
-  for (int i = 0; i < DPL; ++i) o[i] = 0.f;
+  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  const float w_s = lane < S ? __builtin_amdgcn_exp2f(m_s - M) : 0.f;
+  float l = w_s * l_s;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o);
+
+  fvec o = {};
   float al = 0.f;
   for (int s = 0; s < S; ++s) {
-    const float ws = __shfl(w_s, s);
-    const int64_t pr = prow(s);
-#pragma unroll
-    for (int i = 0; i < DPL; ++i) o[i] += ws * A->ws_o[pr * D + lane + 64 * i];
+    const float ws = lane_bcast(w_s, s);
+    const int64_t pr = p0 + s * pstride;
+    o += ws * *(const fvec*)(A->ws_o + pr * D + lane * DPL);
     al += ws * A->ws_l[pr * 64 + lane];
   }
-  const bf16* Bg = (const bf16*)AG.B + g * D;
+  const bf16* Bg = (const bf16*)AG.B + g * D + lane * DPL;
   for (int rho = 0; rho < rank; ++rho) {
-    const float c = __shfl(al, rho);
+    const float c = lane_bcast(al, rho);
+    const bf16* br = Bg + (int64_t)rho * Hkv * D;
 #pragma unroll
-    for (int i = 0; i < DPL; ++i) o[i] += c * (float)Bg[(int64_t)rho * Hkv * D + lane + 64 * i];
+    for (int i = 0; i < DPL; ++i) o[i] += c * (float)br[i];
   }
   const float inv = 1.f / l;
-  bf16* orow = (bf16*)A->O + ((int64_t)(R.q_start + t) * Hq + h) * D;
+  bf16* orow = (bf16*)A->O + ((int64_t)(R.q_start + t) * Hq + h) * D + lane * DPL;
 #pragma unroll
-  for (int i = 0; i < DPL; ++i) orow[lane + 64 * i] = (bf16)(o[i] * inv);
+  for (int i = 0; i < DPL; ++i) orow[i] = (bf16)(o[i] * inv);
 }
 
 }  // namespace
 
-hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, int n_grid, hipStream_t s) {
-  if (head_dim == 128)
-    hipLaunchKernelGGL(fla_attn_bf16<128>, dim3(n_grid), dim3(kThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL(fla_attn_bf16<64>, dim3(n_grid), dim3(kThreads), 0, s, a);
+hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, int max_rank, int n_grid,
+                            hipStream_t s) {
+  const int rb = max_rank > 32 ? 2 : (max_rank > 0 ? 1 : 0);
+#define LRA_LAUNCH(D, RB) \
+  hipLaunchKernelGGL((fla_attn_bf16<D, RB>), dim3(n_grid), dim3(kThreads), 0, s, a)
+  if (head_dim == 128) {
+    if (rb == 0) LRA_LAUNCH(128, 0);
+    else if (rb == 1) LRA_LAUNCH(128, 1);
+    else LRA_LAUNCH(128, 2);
+  } else {
+    if (rb == 0) LRA_LAUNCH(64, 0);
+    else if (rb == 1) LRA_LAUNCH(64, 1);
+    else LRA_LAUNCH(64, 2);
+  }
+#undef LRA_LAUNCH
   return hipGetLastError();
 }
 

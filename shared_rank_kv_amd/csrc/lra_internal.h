@@ -72,7 +72,8 @@ struct PrecomputeArgs {
 };
 
 // Launchers (return the HIP status of the launch).
-hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, int n_grid, hipStream_t s);
+hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, int max_rank, int n_grid,
+                            hipStream_t s);
 hipError_t launch_combine_bf16(const AttnArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgs& a, int head_dim, int n_blocks, hipStream_t s);
 hipError_t launch_precompute_bf16(const PrecomputeArgs& a, hipStream_t s);
