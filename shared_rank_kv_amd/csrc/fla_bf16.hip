@@ -20,9 +20,10 @@
 // caches keep their natural token-major layout in HBM and LDS.
 //
 // When the planner splits a request's key range over several workgroups (to fill the
-// 256 CUs), each writes its unnormalised partial state (m, l, P·V_base, P·L) to the
-// workspace and fla_combine_bf16 merges them and applies B once per row.  Decode is the
-// same kernel with one query per request and many key splits.
+// 256 CUs), each applies B to its own partial state (B is linear) and writes
+// (m, l, P·V_base + (P·L)·B) to the workspace; fla_combine_bf16 then merges the splits
+// with their softmax weights.  Decode is the same kernel with one query per request and
+// many key splits.
 #include "lra_internal.h"
 
 namespace lra {
@@ -344,127 +345,93 @@ __global__ __launch_bounds__(256, 2) void fla_attn_bf16(const AttnArgs args) {
   }
 
   const float l_tot = half_sum(l_run);
+  // ---- epilogue: acc = P·V_base + (P·L)·B_g with B applied once for the row tile; a
+  // whole key range is normalised by l and stored as bf16 O, a key split stores its
+  // unnormalised fp32 state (m, l, acc) for fla_combine_bf16.
+  const float inv = n_split == 1 ? 1.f / l_tot : 1.f;
   if (n_split == 1) {
-    // ---- epilogue: O = P·V_base / l + ((P·L)/l)·B_g, B applied once for the row tile
-    const float inv = 1.f / l_tot;
 #pragma unroll
     for (int i = 0; i < DB; ++i) accV[i] *= inv;
-    if (RB && rank > 0) {   // a rank-0 agent has no B (its pointer may be null)
-      // B_g = B[:, g*D : (g+1)*D] is a "value tile" whose rows are the rank index.
-      load_rows<D, true>((const bf16*)AG.B + g * D, kv_stride, 0, rank, smem + TILE_KV, wave, lane);
-      wait_loads();
-      __syncthreads();
-      if (wave_active) {
-        const int nst = (rank + 15) / 16;
-        for (int st = 0; st < nst; ++st) {
-          const f32x16 lsc = accL[(RB > 1) ? (st >> 1) : 0] * inv;
-          const bf16x8 pf = pfrag(lsc, st & 1);
-          const int key0 = (st >> 1) * 32 + (st & 1) * 16;
+  }
+  if (RB && rank > 0) {   // a rank-0 agent has no B (its pointer may be null)
+    // B_g = B[:, g*D : (g+1)*D] is a "value tile" whose rows are the rank index.
+    load_rows<D, true>((const bf16*)AG.B + g * D, kv_stride, 0, rank, smem + TILE_KV, wave, lane);
+    wait_loads();
+    __syncthreads();
+    if (wave_active) {
+      const int nst = (rank + 15) / 16;
+      for (int st = 0; st < nst; ++st) {
+        const f32x16 lsc = accL[(RB > 1) ? (st >> 1) : 0] * inv;
+        const bf16x8 pf = pfrag(lsc, st & 1);
+        const int key0 = (st >> 1) * 32 + (st & 1) * 16;
 #pragma unroll
-          for (int db = 0; db < DB; ++db)
-            accV[db] = mfma32(vfrag<D>(smem + TILE_KV, off.v[db], key0), pf, accV[db]);
-        }
+        for (int db = 0; db < DB; ++db)
+          accV[db] = mfma32(vfrag<D>(smem + TILE_KV, off.v[db], key0), pf, accV[db]);
       }
     }
-    if (valid) {
-      bf16* orow = (bf16*)A->O + ((int64_t)(q_start + t) * Hq + g * G + hl) * D;
+  }
+  if (!valid) return;
+  if (n_split == 1) {
+    bf16* orow = (bf16*)A->O + ((int64_t)(q_start + t) * Hq + g * G + hl) * D;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          bf16x4 o;
+      for (int i = 0; i < 4; ++i) {
+        bf16x4 o;
 #pragma unroll
-          for (int j2 = 0; j2 < 4; ++j2) o[j2] = (bf16)accV[db][i * 4 + j2];
-          *(bf16x4*)(orow + db * 32 + i * 8 + hi * 4) = o;
-        }
-    }
-  } else if (valid) {
-    // ---- partial state of this key split for the combine pass
+        for (int j2 = 0; j2 < 4; ++j2) o[j2] = (bf16)accV[db][i * 4 + j2];
+        *(bf16x4*)(orow + db * 32 + i * 8 + hi * 4) = o;
+      }
+  } else {
     const int64_t pr = (int64_t)R.part_base + ((int64_t)sp * Lq + t) * Hq + g * G + hl;
     float* po = A->ws_o + pr * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f32x4 v = {accV[db][i * 4], accV[db][i * 4 + 1], accV[db][i * 4 + 2], accV[db][i * 4 + 3]};
-        *(f32x4*)(po + db * 32 + i * 8 + hi * 4) = v;
-      }
-    float* pl = A->ws_l + pr * 64;
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f32x4 v = {};
-        if (rb < RB) v = f32x4{accL[rb][i * 4], accL[rb][i * 4 + 1], accL[rb][i * 4 + 2], accL[rb][i * 4 + 3]};
-        *(f32x4*)(pl + rb * 32 + i * 8 + hi * 4) = v;
-      }
-    if (hi == 0) {
-      A->ws_ml[pr * 2] = m_run;
-      A->ws_ml[pr * 2 + 1] = l_tot;
-    }
+      for (int i = 0; i < 4; ++i)
+        *(f32x4*)(po + db * 32 + i * 8 + hi * 4) =
+            f32x4{accV[db][i * 4], accV[db][i * 4 + 1], accV[db][i * 4 + 2], accV[db][i * 4 + 3]};
+    if (hi == 0) *(float2*)(A->ws_ml + pr * 2) = float2{m_run, l_tot};
   }
 }
 
-// Merge the key-split partial states of one output row (one wave per row):
-//   M = max m_s, w_s = 2^(m_s - M),
-//   O = (Σ w_s·(P·V_base)_s + (Σ w_s·(P·L)_s)·B_g) / Σ w_s·l_s
-// B is linear, so applying it once after the merge equals applying it per split.  A lane
-// owns D/64 consecutive output lanes; split weights and the merged LR row are broadcast
-// with readlane.
+// Merge the key-split states of one output row:
+//   M = max m_s, w_s = 2^(m_s - M),   O = Σ w_s·acc_s / Σ w_s·l_s
+// where acc_s = (P·V_base)_s + (P·L)_s·B_g already holds the up-projection (B is linear).
+// D/4 threads per row, each owning 4 consecutive output lanes.
 template <int D>
 __global__ __launch_bounds__(256) void fla_combine_bf16(const AttnArgs args) {
   const AttnArgs* A = (const AttnArgs*)__builtin_amdgcn_kernarg_segment_ptr();
-  constexpr int DPL = D / 64;
-  typedef float fvec __attribute__((ext_vector_type(DPL)));
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + wave;
+  constexpr int TPR = D / 4, RPB = 256 / TPR;
+  const int row = blockIdx.x * RPB + threadIdx.x / TPR;
+  const int q4 = threadIdx.x % TPR;
   if (row >= A->n_comb) return;
-  int b = -1;
+  int b = 0;
   for (int i = 0; i < A->n_req; ++i)
     if (A->reqs[i].n_split > 1 && A->reqs[i].comb_start <= row) b = i;
   const ReqDesc& R = A->reqs[b];
-  const int Hq = A->Hq, G = A->G, Hkv = A->Hkv;
+  const int Hq = A->Hq;
   const int local = row - R.comb_start;
-  const int t = local / Hq, h = local - t * Hq, g = h / G;
+  const int t = local / Hq, h = local - t * Hq;
   const int S = R.n_split;
-  const AgentDesc& AG = A->agents[R.agent];
-  const int rank = AG.rank;
-  const int64_t p0 = (int64_t)R.part_base + (int64_t)t * Hq + h;   // split s adds s*Lq*Hq
+  const int64_t p0 = (int64_t)R.part_base + (int64_t)t * Hq + h;
   const int64_t pstride = (int64_t)R.q_len * Hq;
-
-  float m_s = kNegBig, l_s = 0.f;
-  if (lane < S) {
-    const float2 ml = *(const float2*)(A->ws_ml + (p0 + lane * pstride) * 2);
-    m_s = ml.x;
-    l_s = ml.y;
-  }
-  float M = m_s;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-  const float w_s = lane < S ? __builtin_amdgcn_exp2f(m_s - M) : 0.f;
-  float l = w_s * l_s;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o);
-
-  fvec o = {};
-  float al = 0.f;
-  for (int s = 0; s < S; ++s) {
-    const float ws = lane_bcast(w_s, s);
-    const int64_t pr = p0 + s * pstride;
-    o += ws * *(const fvec*)(A->ws_o + pr * D + lane * DPL);
-    al += ws * A->ws_l[pr * 64 + lane];
-  }
-  const bf16* Bg = (const bf16*)AG.B + g * D + lane * DPL;
-  for (int rho = 0; rho < rank; ++rho) {
-    const float c = lane_bcast(al, rho);
-    const bf16* br = Bg + (int64_t)rho * Hkv * D;
-#pragma unroll
-    for (int i = 0; i < DPL; ++i) o[i] += c * (float)br[i];
+  float M = kNegBig;
+  for (int s2 = 0; s2 < S; ++s2) M = fmaxf(M, A->ws_ml[(p0 + s2 * pstride) * 2]);
+  float l = 0.f;
+  f32x4 o = {};
+  for (int s2 = 0; s2 < S; ++s2) {
+    const int64_t pr = p0 + s2 * pstride;
+    const float2 ml = *(const float2*)(A->ws_ml + pr * 2);
+    const float w = __builtin_amdgcn_exp2f(ml.x - M);
+    l += w * ml.y;
+    o += w * *(const f32x4*)(A->ws_o + pr * D + q4 * 4);
   }
   const float inv = 1.f / l;
-  bf16* orow = (bf16*)A->O + ((int64_t)(R.q_start + t) * Hq + h) * D + lane * DPL;
+  bf16x4 ob;
 #pragma unroll
-  for (int i = 0; i < DPL; ++i) orow[i] = (bf16)(o[i] * inv);
+  for (int j2 = 0; j2 < 4; ++j2) ob[j2] = (bf16)(o[j2] * inv);
+  *(bf16x4*)((bf16*)A->O + ((int64_t)(R.q_start + t) * Hq + h) * D + q4 * 4) = ob;
 }
 
 }  // namespace
@@ -488,7 +455,8 @@ hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, int max_rank, int n
 }
 
 hipError_t launch_combine_bf16(const AttnArgs& a, int head_dim, hipStream_t s) {
-  const int grid = (a.n_comb + 3) / 4;
+  const int rpb = 256 / (head_dim / 4);
+  const int grid = (a.n_comb + rpb - 1) / rpb;
   if (head_dim == 128)
     hipLaunchKernelGGL(fla_combine_bf16<128>, dim3(grid), dim3(kThreads), 0, s, a);
   else

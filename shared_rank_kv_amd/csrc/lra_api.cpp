@@ -158,10 +158,8 @@ struct Plan {
   size_t ws_bytes = 0;
 };
 
-constexpr int kPartCols = 64;          // ws_l columns (maximum rank)
-
 size_t part_bytes(int64_t part_rows, int D) {
-  return (size_t)part_rows * (size_t)(D + kPartCols + 2) * sizeof(float);
+  return (size_t)part_rows * (size_t)(D + 2) * sizeof(float);
 }
 
 Plan make_plan(const AttnShape& s, bool decode, const int32_t* q_len, const int32_t* k_len) {
@@ -241,8 +239,7 @@ int run_attention(const AttnShape& s, bool decode, const Requests& rq, const voi
   if (p.part_rows) {
     uintptr_t base = (reinterpret_cast<uintptr_t>(ws) + 255) & ~uintptr_t(255);
     a.ws_o = reinterpret_cast<float*>(base);
-    a.ws_l = a.ws_o + p.part_rows * s.D;
-    a.ws_ml = a.ws_l + p.part_rows * kPartCols;
+    a.ws_ml = a.ws_o + p.part_rows * s.D;
   }
   a.Hq = s.Hq;
   a.Hkv = s.Hkv;

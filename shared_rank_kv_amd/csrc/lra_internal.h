@@ -44,9 +44,8 @@ struct AttnArgs {
   const void* K;
   const void* V;
   void* O;
-  float* ws_o;         // [part_rows, D]      unnormalised P·V_base partials
-  float* ws_l;         // [part_rows, 64]     unnormalised P·L partials
-  float* ws_ml;        // [part_rows, 2]      (running max in log2 units, row sum)
+  float* ws_o;         // [part_rows, D]  unnormalised P·V_base + (P·L)·B of a key split
+  float* ws_ml;        // [part_rows, 2]  (running max in log2 units, row sum)
   int32_t Hq, Hkv, G;
   int32_t n_req;
   int32_t n_work;      // work items (workgroups that do work) in this launch
