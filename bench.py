@@ -48,14 +48,16 @@ def _events(n):
 
 
 class Flusher:
-    """Evicts the 256 MB Infinity Cache (MALL) by writing a 512 MB buffer."""
+    """Evicts the 256 MB Infinity Cache (MALL) by reading a 512 MB buffer.  A read leaves
+    clean lines behind; a write-based flush would leave dirty lines whose write-backs
+    then compete with the timed kernel's reads."""
 
     def __init__(self):
         import torch
-        self.buf = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        self.buf = torch.ones(64 << 20, dtype=torch.int64, device="cuda")
 
     def __call__(self):
-        self.buf.fill_(1)
+        self.buf.sum()
 
 
 def time_calls(fn, steps, warmup, flush=None):
@@ -96,14 +98,11 @@ def upload(prob, L=None):
 
 
 def prefill_call(prob, dev, ws):
+    """The C call with its arguments marshalled once (only the call itself is timed)."""
     from shared_rank_kv_amd import lra
-    O = torch_empty_like(dev["Q"])
-
-    def fn():
-        lra.lra_attn_prefill(dev["Q"], dev["K"], dev["V"], dev["L"], dev["B"], prob.q_start,
-                             prob.q_len, prob.k_start, prob.k_len, prob.agent_idx, O=O,
-                             workspace=ws)
-    return fn
+    return lra.prepare_attn_prefill(dev["Q"], dev["K"], dev["V"], dev["L"], dev["B"],
+                                    prob.q_start, prob.q_len, prob.k_start, prob.k_len,
+                                    prob.agent_idx, O=torch_empty_like(dev["Q"]), workspace=ws)
 
 
 def torch_empty_like(t):
@@ -139,11 +138,9 @@ def bench_decode(steps, warmup, flush):
     cpu, dev = upload(prob)
     log(f"[bench] decode inputs ready in {time.time() - t:.1f}s")
     ws = workspace_for(prob, True)
-    O = torch_empty_like(dev["Q"])
-
-    def fn():
-        lra.lra_attn_decode(dev["Q"], dev["K"], dev["V"], dev["L"], dev["B"], prob.k_start,
-                            prob.k_len, prob.agent_idx, O=O, workspace=ws)
+    fn = lra.prepare_attn_decode(dev["Q"], dev["K"], dev["V"], dev["L"], dev["B"], prob.k_start,
+                                 prob.k_len, prob.agent_idx, O=torch_empty_like(dev["Q"]),
+                                 workspace=ws)
     per, _ = time_calls(fn, steps, warmup, flush)
     flop, nbytes = accounting.attention_work(prob)
     del dev, cpu
@@ -162,8 +159,7 @@ def bench_longctx(steps, warmup, flush):
     A_cat = torch.cat([pre.A(a) for a in range(3)], 1).contiguous().cuda()
     Ls = [torch.empty(pre.T, r, dtype=torch.bfloat16, device="cuda") for r in pre.ranks]
 
-    def pfn():
-        lra.lra_precompute_lr(X, A_cat, pre.ranks, Ls)
+    pfn = lra.prepare_precompute_lr(X, A_cat, pre.ranks, Ls)
     per, _ = time_calls(pfn, steps, warmup, flush)
     pflop, pbytes = accounting.precompute_work(pre)
     pms = float(np.median(per))
@@ -172,7 +168,7 @@ def bench_longctx(steps, warmup, flush):
                   "tflops": round(pflop / (pms * 1e-3) / 1e12, 1), "ms_per_call": round(pms, 4),
                   "bytes": pbytes, "flop": pflop,
                   "roofline": roof(pgbs, accounting.PEAK_HBM_GBS, "GB/s", "hbm")}
-    del X
+    del X, pfn
     prob = workloads.longctx_prefill(agents=(0,))
     _, dev = upload(prob, L=Ls)
     ws = workspace_for(prob, False)
@@ -203,16 +199,19 @@ def bench_mixed(steps, warmup):
         layers.append((prob, dev))
     log(f"[bench] mixed-batch inputs (32 layers) ready in {time.time() - t:.1f}s")
 
+    calls = [lra.prepare_attn_prefill(dev["Q"], dev["K"], dev["V"], dev["L"], dev["B"],
+                                      prob.q_start, prob.q_len, prob.k_start, prob.k_len,
+                                      prob.agent_idx, O=dev["O"], workspace=dev["ws"])
+             for prob, dev in layers]
+
     def fn():
-        for prob, dev in layers:
-            lra.lra_attn_prefill(dev["Q"], dev["K"], dev["V"], dev["L"], dev["B"], prob.q_start,
-                                 prob.q_len, prob.k_start, prob.k_len, prob.agent_idx,
-                                 O=dev["O"], workspace=dev["ws"])
+        for c in calls:
+            c()
     per, _ = time_calls(fn, max(3, steps // 4), max(1, warmup // 2))
     ms = float(np.median(per))
     ideal_ms = max(tflop / (accounting.PEAK_BF16_TFLOPS * 1e12),
                    tbytes / (accounting.PEAK_HBM_GBS * 1e9)) * 1e3
-    del layers
+    del layers, calls
     torch.cuda.empty_cache()
     return {"workload": "mixed32-32req-ranks8-16-32-64", "ms_per_32_layers": round(ms, 3),
             "flop": tflop, "bytes": tbytes, "tflops": round(tflop / (ms * 1e-3) / 1e12, 1),

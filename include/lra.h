@@ -84,7 +84,7 @@ enum lra_dtype { LRA_DTYPE_F32 = 0, LRA_DTYPE_BF16 = 1 };
  *            stride ldl[a] elements (>= r_a).  Outputs may be column blocks of one buffer.
  *   ldl      host   [n_agents]
  * Requires d_model % 8 == 0, ldx % 8 == 0, sum(r_a) <= 256, a 16-byte aligned X, and for
- * bf16 also lda % 8 == 0 and a 16-byte aligned A_cat.  Outputs are rounded to the dtype
+ * bf16 also d_model % 64 == 0, lda % 8 == 0 and a 16-byte aligned A_cat.  Outputs are rounded to the dtype
  * (bf16: nearest even) from fp32 accumulation.  T == 0 is a no-op.
  */
 int lra_precompute_lr(int dtype, int64_t T, int64_t d_model,

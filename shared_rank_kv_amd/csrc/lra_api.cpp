@@ -389,6 +389,8 @@ int lra_precompute_lr(int dtype, int64_t T, int64_t d_model, const void* X, int6
     R += ranks[a];
   }
   if (d_model % 8 != 0) return fail(LRA_ERR_UNSUPPORTED, "d_model %lld %% 8 != 0", (long long)d_model);
+  if (dtype == LRA_DTYPE_BF16 && d_model % 64 != 0)
+    return fail(LRA_ERR_UNSUPPORTED, "bf16 d_model %lld %% 64 != 0", (long long)d_model);
   if (ldx < d_model || ldx % 8 != 0)
     return fail(LRA_ERR_INVALID, "ldx %lld must be >= d_model and a multiple of 8", (long long)ldx);
   if (lda < R) return fail(LRA_ERR_INVALID, "lda %lld < sum of ranks %lld", (long long)lda,

@@ -5,13 +5,12 @@
 // bf16 path: a tall-skinny GEMM L_cat[T, R] = X[T, d_model]·A_cat[d_model, R] with
 // R = sum of ranks <= 256.  The work is bound by reading X once from HBM (R = 192 gives
 // ~180 FLOP per byte, under the MI355X ridge), so every workgroup owns 128 rows of X and
-// ALL R columns, and X never passes through LDS: each lane loads its MFMA A-operand
-// fragment (8 consecutive d_model values of one row) straight from HBM into registers,
-// two 64-wide d_model chunks ahead of use.  A_cat chunks (64 x R) are shared by the
-// workgroup through a padded LDS tile and read as B operands with ds_read_b64_tr_b16.
-// Four waves split the 128 x R tile 2 x 2 (64 rows x R/2 columns each) with
-// v_mfma_f32_32x32x16_bf16; the epilogue rounds to bf16 and scatters column blocks to
-// each agent's L_a.
+// ALL R columns, reading X from HBM exactly once.  X chunks (128 rows x 64 d_model values,
+// whole 128-byte row segments per 8-lane group) and A_cat chunks (64 x R) are loaded two
+// chunks ahead into registers and stored into LDS tiles (X swizzled, A_cat padded); the
+// B operands are read with ds_read_b64_tr_b16.  Four waves split the 128 x R tile 2 x 2 (64 rows x R/2 columns
+// each) with v_mfma_f32_32x32x16_bf16; the epilogue rounds to bf16 and scatters column
+// blocks to each agent's L_a.
 //
 // fp32 path: a plain LDS-tiled fp32 GEMM (exactness, not throughput).
 #include "lra_internal.h"
@@ -43,61 +42,93 @@ __device__ __forceinline__ bf16x8 join(i16x4 lo, i16x4 hi) {
 template <int NBW>
 __global__ __launch_bounds__(256, 1) void lr_precompute_bf16(const PrecomputeArgs args) {
   const PrecomputeArgs* P = (const PrecomputeArgs*)__builtin_amdgcn_kernarg_segment_ptr();
-  constexpr int NBT = 2 * NBW;                 // 32-column blocks in the padded tile
-  constexpr int RS = NBT * 32 * 2 + 16;        // LDS row stride (bytes), padded
-  constexpr int CHUNKS = KC * NBT * 4;         // 16-byte chunks of one A_cat tile
-  constexpr int CPT = CHUNKS / 256;            // per thread (= NBT)
-  __shared__ __attribute__((aligned(16))) char smem_raw[2 * KC * RS];
-  LDS char* smem = (LDS char*)smem_raw;
+  constexpr int NBT = 2 * NBW;                 // 32-column blocks in the padded A_cat tile
+  constexpr int RS = NBT * 32 * 2 + 16;        // A_cat LDS row stride (bytes), padded
+  constexpr int CPT = NBT;                     // 16-byte A_cat chunks per thread per tile
+  constexpr int XS = 2;                        // X LDS stages
+  constexpr int XTILE = TM * KC * 2;           // 16 KB: 128 rows x 64 d_model values
+  constexpr int UX = XTILE / 1024 / 4;         // X direct loads per wave per chunk (4)
+  constexpr int ATILE = KC * RS;
+  __shared__ __attribute__((aligned(1024))) char smem_raw[XS * XTILE + 2 * ATILE];
+  LDS char* xlds = (LDS char*)smem_raw;
+  LDS char* alds = xlds + XS * XTILE;
 
-  const int tile = blockIdx.x;
-  const int64_t row0 = (int64_t)tile * TM;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int wm = wave & 1, wn = wave >> 1;
   const int hi = lane >> 5;
-  const int64_t T = P->T, dm = P->d_model, ldx = P->ldx, lda = P->lda;
+  const int64_t T = P->T, ldx = P->ldx, lda = P->lda;
   const int R = P->R;
-  const int nk = (int)((dm + KC - 1) / KC);
-  const bf16* X = (const bf16*)P->X;
-  const bf16* Ac = (const bf16*)P->A;
+  const int nk = (int)(P->d_model / KC);       // d_model % 64 == 0 (checked by the host)
+  const int nk_pad = (nk + 1) / 2 * 2;         // padded chunks meet zero rows of A_cat
+  const int64_t row0 = (int64_t)blockIdx.x * TM;
 
-  // X fragments: xs[stage][mb][ks], lane = (row lane&31 of m-block mb, k-half hi)
-  bf16x8 xs[3][2][4];
-  int64_t xrow[2];
-  bool xok[2];
+  // X chunk (128 rows x 128 bytes): each lane loads 16-byte units, 8 whole rows per wave
+  // instruction, two chunks ahead into registers, and stores them into an LDS tile where
+  // unit p of row r holds global unit p ^ ((r >> 1) & 7); that makes the operand reads
+  // below (32 consecutive rows at one unit) bank-conflict free.  Rows past T repeat row T-1
+  // (their results are never stored).  (Register staging measured faster here than direct
+  // global->LDS loads.)
+  const char* xsrc[UX];
+#pragma unroll
+  for (int i = 0; i < UX; ++i) {
+    const int u = wave + 4 * i;
+    const int row = u * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ ((row >> 1) & 7);
+    xsrc[i] = (const char*)P->X + (min(row0 + row, T - 1) * ldx + c * 8) * 2;
+  }
+  // Workgroups start their d_model sweep at different chunks so that they do not all read
+  // the same 128-byte column of the 8 KB rows at once.
+  const int rot = (int)(blockIdx.x % nk);
+  auto chunk = [&](int kc) { return kc < nk ? (kc + rot) % nk : nk - 1; };
+  u32x4 xr[2][UX];
+  auto load_x = [&](u32x4 (&dst)[UX], int kc) {
+    const int64_t koff = (int64_t)chunk(kc) * KC * 2;
+#pragma unroll
+    for (int i = 0; i < UX; ++i) dst[i] = *(const u32x4*)(xsrc[i] + koff);
+  };
+  auto store_x = [&](const u32x4 (&src)[UX], int kc) {
+    LDS char* dst = xlds + (kc % XS) * XTILE;
+#pragma unroll
+    for (int i = 0; i < UX; ++i) *(LDS u32x4*)(dst + (wave + 4 * i) * 1024 + lane * 16) = src[i];
+  };
+  // A operand (row lane&31 of m-block mb, d_model values ks*16 + hi*8 ..) from the X tile
+  int xoff[2][4];
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
-    const int64_t r = row0 + wm * 64 + mb * 32 + (lane & 31);
-    xok[mb] = r < T;
-    xrow[mb] = xok[mb] ? r : 0;
+    const int row = wm * 64 + mb * 32 + (lane & 31);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) xoff[mb][ks] = row * 128 + (((2 * ks + hi) ^ ((row >> 1) & 7)) << 4);
   }
-  auto load_x = [&](bf16x8 (&dst)[2][4], int kc) {
+  // A_cat tile (64 d_model rows x NBT*32 columns), staged through registers into a padded
+  // LDS tile; columns past R and padded chunks are stored as zeros.
+  u32x4 areg[2][CPT];
+  uint32_t aoff[CPT];
+  int a_ok[CPT], lds_off[CPT];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+  for (int i = 0; i < CPT; ++i) {
+    const int ch = tid + 256 * i;
+    const int k = ch / (NBT * 4), c = ch % (NBT * 4);
+    a_ok[i] = c * 8 < R;
+    aoff[i] = (uint32_t)((k * lda + min(c, R / 8 - 1) * 8) * 2);
+    lds_off[i] = k * RS + c * 16;
+  }
+  const char* Abase = (const char*)P->A;
+  auto load_a = [&](u32x4 (&dst)[CPT], int kc) {
+    const char* base = Abase + (int64_t)chunk(kc) * KC * lda * 2;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int64_t k = (int64_t)kc * KC + ks * 16 + hi * 8;
-        dst[mb][ks] = (xok[mb] && k < dm) ? *(const bf16x8*)(X + xrow[mb] * ldx + k) : bf16x8{};
-      }
+    for (int i = 0; i < CPT; ++i) dst[i] = *(const u32x4*)(base + aoff[i]);
   };
-  u32x4 areg[CPT];
-  auto load_a = [&](int kc) {
+  auto store_a = [&](const u32x4 (&src)[CPT], int buf, int kc) {
+    const bool chunk_ok = kc < nk;
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int ch = tid + 256 * i;
-      const int k = ch / (NBT * 4), c = ch % (NBT * 4);
-      const int64_t kk = (int64_t)kc * KC + k;
-      areg[i] = (kk < dm && c * 8 < R) ? *(const u32x4*)(Ac + kk * lda + c * 8) : u32x4{};
-    }
+    for (int i = 0; i < CPT; ++i)
+      *(LDS u32x4*)(alds + buf * ATILE + lds_off[i]) = (chunk_ok && a_ok[i]) ? src[i] : u32x4{};
   };
-  auto store_a = [&](int buf) {
+  const int g16 = lane >> 4, jj = lane & 15;
+  int boff[NBW];
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int ch = tid + 256 * i;
-      const int k = ch / (NBT * 4), c = ch % (NBT * 4);
-      *(LDS u32x4*)(smem + buf * KC * RS + k * RS + c * 16) = areg[i];
-    }
-  };
+  for (int nb = 0; nb < NBW; ++nb)
+    boff[nb] = ((g16 >> 1) * 8 + (jj >> 2)) * RS + ((wn * NBW + nb) * 32 + (g16 & 1) * 16 + (jj & 3) * 4) * 2;
 
   f32x16 acc[2][NBW];
 #pragma unroll
@@ -105,39 +136,42 @@ __global__ __launch_bounds__(256, 1) void lr_precompute_bf16(const PrecomputeArg
 #pragma unroll
     for (int nb = 0; nb < NBW; ++nb) acc[mb][nb] = f32x16{};
 
-  load_a(0);
-  load_x(xs[0], 0);
-  if (nk > 1) load_x(xs[1], 1);
-  store_a(0);
+  load_a(areg[0], 0);
+  load_x(xr[0], 0);
+  load_a(areg[1], 1);
+  load_x(xr[1], 1);
+  store_a(areg[0], 0, 0);
+  store_x(xr[0], 0);
   __syncthreads();
 
-  const int g16 = lane >> 4, jj = lane & 15;
-  for (int kc0 = 0; kc0 < nk; kc0 += 3) {
+  for (int kc0 = 0; kc0 < nk_pad; kc0 += 2) {
 #pragma unroll
-    for (int st = 0; st < 3; ++st) {
+    for (int st = 0; st < 2; ++st) {
       const int kc = kc0 + st;
-      if (kc < nk) {
-        if (kc + 2 < nk) load_x(xs[(st + 2) % 3], kc + 2);
-        if (kc + 1 < nk) load_a(kc + 1);
-        const LDS char* at = smem + (kc & 1) * KC * RS;
+      // both operands two chunks ahead, into the register slots freed last iteration
+      load_a(areg[st & 1], kc + 2);
+      load_x(xr[st & 1], kc + 2);
+      const LDS char* xt = xlds + (kc % XS) * XTILE;
+      const LDS char* at = alds + (kc & 1) * ATILE;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
+      for (int ks = 0; ks < 4; ++ks) {
+        bf16x8 af[2], bf[NBW];
 #pragma unroll
-          for (int nb = 0; nb < NBW; ++nb) {
-            const int n = (wn * NBW + nb) * 32 + (g16 & 1) * 16 + (jj & 3) * 4;
-            const int k = ks * 16 + (g16 >> 1) * 8 + (jj >> 2);
-            i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS i16x4*)(at + k * RS + n * 2));
-            i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS i16x4*)(at + (k + 4) * RS + n * 2));
-            const bf16x8 bf = join(lo, hi4);
+        for (int mb = 0; mb < 2; ++mb) af[mb] = *(const LDS bf16x8*)(xt + xoff[mb][ks]);
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb) acc[mb][nb] = mfma32(xs[st][mb][ks], bf, acc[mb][nb]);
-          }
+        for (int nb = 0; nb < NBW; ++nb) {
+          const LDS char* p = at + boff[nb] + ks * 16 * RS;
+          bf[nb] = join(__builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS i16x4*)p),
+                        __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS i16x4*)(p + 4 * RS)));
         }
-        if (kc + 1 < nk) {
-          store_a((kc + 1) & 1);
-        }
-        __syncthreads();
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < NBW; ++nb) acc[mb][nb] = mfma32(af[mb], bf[nb], acc[mb][nb]);
       }
+      store_a(areg[(st + 1) & 1], (kc + 1) & 1, kc + 1);
+      store_x(xr[(st + 1) & 1], kc + 1);
+      __syncthreads();
     }
   }
 

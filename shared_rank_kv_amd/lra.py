@@ -132,8 +132,22 @@ def _workspace(nbytes, device, workspace):
     return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
 
 
-def lra_precompute_lr(X, A_cat, ranks, L_out, stream=None):
-    """L_out[a] <- X · A_cat[:, off_a:off_a + ranks[a]] (PreLRShared precompute).
+class Prepared:
+    """A marshalled call: the ctypes arguments (and the host arrays and tensors they point
+    to) are built once; calling it only runs the C entry point on the current stream."""
+
+    def __init__(self, cfn, args, keep, result, stream_index):
+        self._cfn, self._args, self._keep, self.result = cfn, list(args), keep, result
+        self._si = stream_index
+
+    def __call__(self, stream=None):
+        self._args[self._si] = _stream(stream)
+        _check(self._cfn(*self._args))
+        return self.result
+
+
+def prepare_precompute_lr(X, A_cat, ranks, L_out):
+    """Prepared lra_precompute_lr: L_out[a] <- X · A_cat[:, off_a:off_a + ranks[a]].
 
     X [T, d_model], A_cat [d_model, sum(ranks)] (row strides may exceed the widths),
     L_out: list of [T, r_a] GPU tensors (row stride = stride(0)).
@@ -141,22 +155,21 @@ def lra_precompute_lr(X, A_cat, ranks, L_out, stream=None):
     _dtype(X)
     assert X.dim() == 2 and A_cat.dim() == 2 and X.stride(1) == 1 and A_cat.stride(1) == 1
     rk, rkp = _i32(ranks)
-    keep, ptrs = _ptrs(L_out)
+    pk, ptrs = _ptrs(L_out)
     ld, ldp = _i64([t.stride(0) for t in L_out])
-    rc = lib.lra_precompute_lr(_dtype(X), X.shape[0], X.shape[1], X.data_ptr(), X.stride(0),
-                               A_cat.data_ptr(), A_cat.stride(0), len(rk), rkp, ptrs, ldp,
-                               _stream(stream))
-    _check(rc)
-    return L_out
+    args = (_dtype(X), X.shape[0], X.shape[1], X.data_ptr(), X.stride(0), A_cat.data_ptr(),
+            A_cat.stride(0), len(rk), rkp, ptrs, ldp, None)
+    return Prepared(lib.lra_precompute_lr, args, (X, A_cat, L_out, rk, pk, ld), L_out, 11)
 
 
-def lra_attn_prefill(Q, K_base, V_base, L, B, q_start, q_len, k_start, k_len, agent_idx, O=None,
-                     workspace=None, stream=None):
-    """Flash-LoRA-Attention over a batch of requests; returns O [q_rows, Hq, D].
+def lra_precompute_lr(X, A_cat, ranks, L_out, stream=None):
+    """L_out[a] <- X · A_cat[:, off_a:off_a + ranks[a]] (PreLRShared precompute)."""
+    return prepare_precompute_lr(X, A_cat, ranks, L_out)(stream)
 
-    Q [q_rows, Hq, D]; K_base, V_base [kv_rows, Hkv, D]; L: list of per-agent [kv_rows, r_a]
-    LR caches (row stride may exceed r_a; None for rank 0); B: list of [r_a, Hkv*D].
-    """
+
+def prepare_attn_prefill(Q, K_base, V_base, L, B, q_start, q_len, k_start, k_len, agent_idx,
+                         O=None, workspace=None):
+    """Prepared lra_attn_prefill (see lra_attn_prefill)."""
     _dev(Q, "Q"), _dev(K_base, "K_base"), _dev(V_base, "V_base")
     dt = _dtype(Q)
     q_rows, Hq, D = Q.shape
@@ -175,20 +188,29 @@ def lra_attn_prefill(Q, K_base, V_base, L, B, q_start, q_len, k_start, k_len, ag
     bk, bp = _ptrs(B)
     need = lib.lra_attn_workspace_bytes(dt, 0, len(ql), qlp, klp, Hq, Hkv, D, max(ranks + [0]))
     if need == ctypes.c_size_t(-1).value:
-        need = 0      # invalid arguments: the call below reports why
+        need = 0      # invalid arguments: the call reports why
     ws, ws_bytes = _workspace(need, Q.device, workspace)
-    rc = lib.lra_attn_prefill(dt, len(ql), Hq, Hkv, D, qsp, qlp, ksp, klp, agp, Q.data_ptr(), q_rows,
-                              K_base.data_ptr(), V_base.data_ptr(), kv_rows, len(rk), rkp, lp, ldp,
-                              bp, O.data_ptr(), ws.data_ptr() if ws is not None else None, ws_bytes,
-                              _stream(stream))
-    _check(rc)
-    return O
+    args = (dt, len(ql), Hq, Hkv, D, qsp, qlp, ksp, klp, agp, Q.data_ptr(), q_rows,
+            K_base.data_ptr(), V_base.data_ptr(), kv_rows, len(rk), rkp, lp, ldp, bp,
+            O.data_ptr(), ws.data_ptr() if ws is not None else None, ws_bytes, None)
+    keep = (Q, K_base, V_base, L, B, O, ws, qs, ql, ks, kl, ag, rk, lk, ld, bk)
+    return Prepared(lib.lra_attn_prefill, args, keep, O, 23)
 
 
-def lra_attn_decode(Q, K_base, V_base, L, B, k_start, k_len, agent_idx, O=None, workspace=None,
-                    stream=None):
-    """One query token per request: Q, O [batch, Hq, D]; request b attends to key rows
-    [k_start[b], k_start[b] + k_len[b]) of its agent."""
+def lra_attn_prefill(Q, K_base, V_base, L, B, q_start, q_len, k_start, k_len, agent_idx, O=None,
+                     workspace=None, stream=None):
+    """Flash-LoRA-Attention over a batch of requests; returns O [q_rows, Hq, D].
+
+    Q [q_rows, Hq, D]; K_base, V_base [kv_rows, Hkv, D]; L: list of per-agent [kv_rows, r_a]
+    LR caches (row stride may exceed r_a; None for rank 0); B: list of [r_a, Hkv*D].
+    """
+    return prepare_attn_prefill(Q, K_base, V_base, L, B, q_start, q_len, k_start, k_len,
+                                agent_idx, O, workspace)(stream)
+
+
+def prepare_attn_decode(Q, K_base, V_base, L, B, k_start, k_len, agent_idx, O=None,
+                        workspace=None):
+    """Prepared lra_attn_decode (see lra_attn_decode)."""
     _dev(Q, "Q"), _dev(K_base, "K_base"), _dev(V_base, "V_base")
     dt = _dtype(Q)
     batch, Hq, D = Q.shape
@@ -207,8 +229,16 @@ def lra_attn_decode(Q, K_base, V_base, L, B, k_start, k_len, agent_idx, O=None, 
     if need == ctypes.c_size_t(-1).value:
         need = 0
     ws, ws_bytes = _workspace(need, Q.device, workspace)
-    rc = lib.lra_attn_decode(dt, batch, Hq, Hkv, D, ksp, klp, agp, Q.data_ptr(), K_base.data_ptr(),
-                             V_base.data_ptr(), kv_rows, len(rk), rkp, lp, ldp, bp, O.data_ptr(),
-                             ws.data_ptr() if ws is not None else None, ws_bytes, _stream(stream))
-    _check(rc)
-    return O
+    args = (dt, batch, Hq, Hkv, D, ksp, klp, agp, Q.data_ptr(), K_base.data_ptr(),
+            V_base.data_ptr(), kv_rows, len(rk), rkp, lp, ldp, bp, O.data_ptr(),
+            ws.data_ptr() if ws is not None else None, ws_bytes, None)
+    keep = (Q, K_base, V_base, L, B, O, ws, ks, kl, ag, rk, lk, ld, bk)
+    return Prepared(lib.lra_attn_decode, args, keep, O, 20)
+
+
+def lra_attn_decode(Q, K_base, V_base, L, B, k_start, k_len, agent_idx, O=None, workspace=None,
+                    stream=None):
+    """One query token per request: Q, O [batch, Hq, D]; request b attends to key rows
+    [k_start[b], k_start[b] + k_len[b]) of its agent."""
+    return prepare_attn_decode(Q, K_base, V_base, L, B, k_start, k_len, agent_idx, O,
+                               workspace)(stream)

@@ -173,6 +173,7 @@ def _precompute(dtype=lra.LRA_DTYPE_BF16, T=100, dm=64, X=FAKE, ldx=64, A=FAKE, 
     (dict(T=-1), lra.LRA_ERR_INVALID, "T"),
     (dict(dm=0), lra.LRA_ERR_INVALID, "d_model"),
     (dict(dm=60, ldx=64), lra.LRA_ERR_UNSUPPORTED, "d_model"),
+    (dict(dm=72, ldx=72), lra.LRA_ERR_UNSUPPORTED, "% 64"),
     (dict(ldx=32), lra.LRA_ERR_INVALID, "ldx"),
     (dict(lda=16), lra.LRA_ERR_INVALID, "lda"),
     (dict(lda=28), lra.LRA_ERR_INVALID, "lda"),
