@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(CSRC, "_build")
 LIB = os.path.join(PKG, "liblra.so")
-SOURCES = ["lra_api.cpp", "fla_bf16.hip", "fla_f32.hip", "precompute.hip"]
+SOURCES = ["lra_api.cpp", "fla_bf16.hip", "fla_decode.hip", "fla_f32.hip", "precompute.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

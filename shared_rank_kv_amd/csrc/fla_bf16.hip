@@ -416,16 +416,32 @@ __global__ __launch_bounds__(256) void fla_combine_bf16(const AttnArgs args) {
   const int S = R.n_split;
   const int64_t p0 = (int64_t)R.part_base + (int64_t)t * Hq + h;
   const int64_t pstride = (int64_t)R.q_len * Hq;
-  float M = kNegBig;
-  for (int s2 = 0; s2 < S; ++s2) M = fmaxf(M, A->ws_ml[(p0 + s2 * pstride) * 2]);
-  float l = 0.f;
+  // splits are merged 8 at a time, with all 8 loads in flight before the first is used
+  float M = kNegBig, l = 0.f;
   f32x4 o = {};
-  for (int s2 = 0; s2 < S; ++s2) {
-    const int64_t pr = p0 + s2 * pstride;
-    const float2 ml = *(const float2*)(A->ws_ml + pr * 2);
-    const float w = __builtin_amdgcn_exp2f(ml.x - M);
-    l += w * ml.y;
-    o += w * *(const f32x4*)(A->ws_o + pr * D + q4 * 4);
+  for (int s0 = 0; s0 < S; s0 += 8) {
+    float2 ml[8];
+    f32x4 v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int64_t pr = p0 + (int64_t)min(s0 + i, S - 1) * pstride;
+      ml[i] = *(const float2*)(A->ws_ml + pr * 2);
+      v[i] = *(const f32x4*)(A->ws_o + pr * D + q4 * 4);
+    }
+    float Mc = M;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (s0 + i < S) Mc = fmaxf(Mc, ml[i].x);
+    const float sc = __builtin_amdgcn_exp2f(M - Mc);
+    l *= sc;
+    o *= sc;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float w = s0 + i < S ? __builtin_amdgcn_exp2f(ml[i].x - Mc) : 0.f;
+      l += w * ml[i].y;
+      o += w * v[i];
+    }
+    M = Mc;
   }
   const float inv = 1.f / l;
   bf16x4 ob;

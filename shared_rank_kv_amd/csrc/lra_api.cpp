@@ -282,7 +282,8 @@ int run_attention(const AttnShape& s, bool decode, const Requests& rq, const voi
       a.grid_per_xcd = grid / 8;
       int max_rank = 0;
       for (size_t i = c0; i < c1; ++i) max_rank = std::max(max_rank, ad.ranks[rq.agent[p.active[i]]]);
-      e = lra::launch_attn_bf16(a, s.D, max_rank, grid, stream);
+      e = decode ? lra::launch_decode_bf16(a, s.D, max_rank, grid, stream)
+                 : lra::launch_attn_bf16(a, s.D, max_rank, grid, stream);
       if (e == hipSuccess && comb > 0) e = lra::launch_combine_bf16(a, s.D, stream);
     } else {
       a.grid_per_xcd = 0;

@@ -27,8 +27,9 @@ struct AgentDesc {
   int32_t pad_;
 };
 
-// One request of a launch.  Work items of a request are numbered
-// ((g * n_split + split) * n_rt + rt) with rt (row tile) fastest.
+// One request of a launch.  In the prefill kernel the work items of a request are
+// numbered ((g * n_split + split) * n_rt + rt) with rt (row tile) fastest; in the decode
+// kernel (n_rt = 1) they are numbered (split * Hkv + g).
 struct ReqDesc {
   int32_t q_start, q_len, k_start, k_len;
   int32_t agent;
@@ -73,6 +74,8 @@ struct PrecomputeArgs {
 // Launchers (return the HIP status of the launch).
 hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, int max_rank, int n_grid,
                             hipStream_t s);
+hipError_t launch_decode_bf16(const AttnArgs& a, int head_dim, int max_rank, int n_grid,
+                              hipStream_t s);
 hipError_t launch_combine_bf16(const AttnArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgs& a, int head_dim, int n_blocks, hipStream_t s);
 hipError_t launch_precompute_bf16(const PrecomputeArgs& a, hipStream_t s);

@@ -153,6 +153,28 @@ def test_bf16_decode_split_counts(chunk, monkeypatch):
     _cmp_full(prob, cpu, H.run_decode(prob, dev))
 
 
+# (D, Hq, Hkv, ranks, k_len, agents): group sizes 1, 2, 4 and 8, rank-0 agents next to
+# rank-64 ones (the LR tile of a rank-0 agent stays zero and its B is never read), key
+# counts around the 32-key wave tile and the 128-key workgroup round.
+DECODE_SHAPES = [
+    (128, 8, 1, (0, 64), [1, 31, 32, 33, 127, 128, 129, 3000], [0, 1, 0, 1, 0, 1, 0, 1]),
+    (128, 4, 4, (24,), [7, 500, 2049], [0, 0, 0]),
+    (64, 16, 2, (64, 0, 40), [96, 1, 700, 4100], [0, 1, 2, 2]),
+    (64, 8, 2, (0,), [200, 65], [0, 0]),
+]
+
+
+@pytest.mark.parametrize("shape", DECODE_SHAPES, ids=lambda s: f"D{s[0]}-Hq{s[1]}-Hkv{s[2]}-r{max(s[3])}")
+@pytest.mark.parametrize("chunk", ["64", "1024"])
+def test_bf16_decode_shapes(shape, chunk, monkeypatch):
+    monkeypatch.setenv("LRA_DECODE_CHUNK", chunk)
+    D, Hq, Hkv, ranks, k_len, agents = shape
+    prob = workloads.custom("bf16-decode-shape", "bf16", Hq, Hkv, D, ranks, [1] * len(k_len),
+                            k_len, agents, seed=670 + D + Hq)
+    cpu, dev = H.device_inputs(prob)
+    _cmp_full(prob, cpu, H.run_decode(prob, dev))
+
+
 # ---------------------------------------------------------------------------------------
 # LR precompute
 # ---------------------------------------------------------------------------------------
