@@ -24,7 +24,7 @@
 // (m, l, P·V_base + (P·L)·B) to the workspace; fla_combine_bf16 then merges the splits
 // with their softmax weights.  Decode is the same kernel with one query per request and
 // many key splits.
-#include "lra_internal.h"
+#include "lra_device.h"
 
 namespace lra {
 namespace {
@@ -187,8 +187,7 @@ __global__ __launch_bounds__(256, 2) void fla_attn_bf16(const AttnArgs args) {
   const int bid = blockIdx.x;
   const int w = (bid & 7) * A->grid_per_xcd + (bid >> 3);
   if (w >= A->n_work) return;
-  int b = 0;
-  while (b + 1 < A->n_req && A->reqs[b + 1].work_start <= w) ++b;
+  const int b = find_request(A, w);
   const ReqDesc& R = A->reqs[b];
   const int q_start = R.q_start, Lq = R.q_len, k_start = R.k_start, Lk = R.k_len;
   const int n_rt = R.n_rt, n_split = R.n_split;
@@ -405,10 +404,8 @@ __global__ __launch_bounds__(256) void fla_combine_bf16(const AttnArgs args) {
   constexpr int TPR = D / 4, RPB = 256 / TPR;
   const int row = blockIdx.x * RPB + threadIdx.x / TPR;
   const int q4 = threadIdx.x % TPR;
+  const int b = find_combine_request(A, min(row, A->n_comb - 1));   // whole wave
   if (row >= A->n_comb) return;
-  int b = 0;
-  for (int i = 0; i < A->n_req; ++i)
-    if (A->reqs[i].n_split > 1 && A->reqs[i].comb_start <= row) b = i;
   const ReqDesc& R = A->reqs[b];
   const int Hq = A->Hq;
   const int local = row - R.comb_start;

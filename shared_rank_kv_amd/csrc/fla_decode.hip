@@ -19,7 +19,7 @@
 // At the end the four wave states are merged through LDS, B_g is applied once
 // (B is linear), and the key split's state (m, l, P·V_base + (P·L)·B) goes to the
 // workspace for fla_combine_bf16, or O is written when the request has one split.
-#include "lra_internal.h"
+#include "lra_device.h"
 
 namespace lra {
 namespace {
@@ -90,8 +90,7 @@ __global__ __launch_bounds__(256, 2) void fla_decode_bf16(const AttnArgs args) {
   const int bid = blockIdx.x;
   const int w = (bid & 7) * A->grid_per_xcd + (bid >> 3);
   if (w >= A->n_work) return;
-  int b = 0;
-  while (b + 1 < A->n_req && A->reqs[b + 1].work_start <= w) ++b;
+  const int b = find_request(A, w);
   const ReqDesc& R = A->reqs[b];
   const int k_start = R.k_start, Lk = R.k_len, n_split = R.n_split;
   const int G = A->G, Hq = A->Hq, Hkv = A->Hkv;

@@ -6,7 +6,7 @@
 // Workgroup = 256 threads = 64 query rows of one (request, q head) x 4 threads per row;
 // each thread holds a quarter of the row's head_dim lanes and of its LR accumulator.
 // K/V_base/L tiles of 32 keys are staged in LDS; scores use accurate expf.
-#include "lra_internal.h"
+#include "lra_device.h"
 
 namespace lra {
 namespace {
@@ -23,8 +23,7 @@ __global__ __launch_bounds__(256) void fla_attn_f32(const AttnArgs args) {
   __shared__ float rowL[64][65];
 
   const int w = blockIdx.x;
-  int b = 0;
-  while (b + 1 < A->n_req && A->reqs[b + 1].work_start <= w) ++b;
+  const int b = find_request(A, w);
   const ReqDesc& R = A->reqs[b];
   const int local = w - R.work_start;
   const int rt = local % R.n_rt, h = local / R.n_rt;
