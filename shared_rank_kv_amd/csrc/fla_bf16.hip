@@ -179,8 +179,13 @@ __global__ __launch_bounds__(256, 2) void fla_attn_bf16(const AttnArgs args) {
   constexpr int TILE_KV = 64 * D * 2;  // bytes of one K or V tile
   constexpr int TILE_L = 64 * 64 * 2;  // bytes of one LR tile (64 x 64 bf16)
   constexpr int BUF = 2 * TILE_KV + TILE_L;
-  __shared__ __attribute__((aligned(1024))) char smem_raw[2 * BUF];
-  LDS char* smem = (LDS char*)smem_raw;
+  // two statically distinct buffers: with the loop unrolled by two, every LDS read names
+  // the buffer it reads and the compiler can tell it apart from the tile being loaded
+  __shared__ __attribute__((aligned(1024))) char smem_a[BUF];
+  __shared__ __attribute__((aligned(1024))) char smem_b[BUF];
+  LDS char* const buf_a = (LDS char*)smem_a;
+  LDS char* const buf_b = (LDS char*)smem_b;
+  LDS char* smem = buf_a;
 
   // ---- work item -> (request, kv head, key split, row tile); XCD-major numbering keeps
   // the row tiles of one (request, kv head, split) on one XCD, sharing its L2.
@@ -253,8 +258,8 @@ __global__ __launch_bounds__(256, 2) void fla_attn_bf16(const AttnArgs args) {
     const f32x4 z = {};
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      *(LDS f32x4*)(smem + 2 * TILE_KV + tid * 32 + i * 16) = z;
-      *(LDS f32x4*)(smem + BUF + 2 * TILE_KV + tid * 32 + i * 16) = z;
+      *(LDS f32x4*)(buf_a + 2 * TILE_KV + tid * 32 + i * 16) = z;
+      *(LDS f32x4*)(buf_b + 2 * TILE_KV + tid * 32 + i * 16) = z;
     }
     __syncthreads();
   }
@@ -266,11 +271,9 @@ __global__ __launch_bounds__(256, 2) void fla_attn_bf16(const AttnArgs args) {
   wait_loads();
   __syncthreads();
 
-  for (int j = 0; j < n_tiles; ++j) {
+  auto tile = [&](const int j, const LDS char* cur, LDS char* nxt) {
     const int k0 = kb + j * kTileKeys;
-    const LDS char* cur = smem + (j & 1) * BUF;
     if (j + 1 < n_tiles) {
-      LDS char* nxt = smem + ((j + 1) & 1) * BUF;
       load_rows<D, false>(Kg, kv_stride, k0 + kTileKeys, ke, nxt, wave, lane);
       load_rows<D, true>(Vg, kv_stride, k0 + kTileKeys, ke, nxt + TILE_KV, wave, lane);
       if (RB) load_lr(Lg, AG.ldl, rank, k0 + kTileKeys, ke, nxt + 2 * TILE_KV, wave, lane);
@@ -341,6 +344,10 @@ __global__ __launch_bounds__(256, 2) void fla_attn_bf16(const AttnArgs args) {
     }
     wait_loads();
     __syncthreads();
+  };
+  for (int j = 0; j < n_tiles; j += 2) {
+    tile(j, buf_a, buf_b);
+    if (j + 1 < n_tiles) tile(j + 1, buf_b, buf_a);
   }
 
   const float l_tot = half_sum(l_run);
@@ -421,20 +428,23 @@ __global__ __launch_bounds__(256) void fla_combine_bf16(const AttnArgs args) {
     f32x4 v[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int64_t pr = p0 + (int64_t)min(s0 + i, S - 1) * pstride;
-      ml[i] = *(const float2*)(A->ws_ml + pr * 2);
-      v[i] = *(const f32x4*)(A->ws_o + pr * D + q4 * 4);
+      const int64_t pr = p0 + (int64_t)(s0 + i) * pstride;
+      ml[i] = float2{kNegBig, 0.f};
+      v[i] = f32x4{};
+      if (s0 + i < S) {
+        ml[i] = *(const float2*)(A->ws_ml + pr * 2);
+        v[i] = *(const f32x4*)(A->ws_o + pr * D + q4 * 4);
+      }
     }
     float Mc = M;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (s0 + i < S) Mc = fmaxf(Mc, ml[i].x);
+    for (int i = 0; i < 8; ++i) Mc = fmaxf(Mc, ml[i].x);
     const float sc = __builtin_amdgcn_exp2f(M - Mc);
     l *= sc;
     o *= sc;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float w = s0 + i < S ? __builtin_amdgcn_exp2f(ml[i].x - Mc) : 0.f;
+      const float w = __builtin_amdgcn_exp2f(ml[i].x - Mc);   // 0 for absent splits
       l += w * ml[i].y;
       o += w * v[i];
     }
