@@ -27,11 +27,16 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           # packed fp32 VALU ops are kept out of the device code (see the design notes)
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Wno-unused-result"]
+# The attention kernels take no NaN inputs (masked scores are -inf, never NaN).  With the
+# IEEE mode bit off, v_max_f32 needs no quieting of signalling NaNs, so the softmax row max
+# does not canonicalise every MFMA result first.
+EXTRA = {"fla_bf16.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
+         "fla_decode.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}
 
 
 def _compile(src):
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd = [HIPCC, "-x", "hip", *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)

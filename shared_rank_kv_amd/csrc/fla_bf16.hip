@@ -80,42 +80,49 @@ __device__ __forceinline__ int swz_k(int row) { return D == 128 ? (row & 15) : (
 template <int D>
 __device__ __forceinline__ int swz_v(int row) { return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1); }
 
-// 64 rows x D bf16 from a strided source into LDS with direct global->LDS loads.  Rows at
-// or past `valid` repeat row valid-1 so the tile holds only finite data (the caller masks
-// them out).  Each wave writes 1 KB units u = wave, wave+4, ...
-template <int D, bool VSWZ>
-__device__ __forceinline__ void load_rows(const bf16* src, int64_t stride, int r0, int valid,
-                                          LDS char* dst, int wave, int lane) {
-  constexpr int CPR = D / 8;
-  constexpr int RPU = 64 / CPR;        // rows per 1 KB unit
-  constexpr int UNITS = 64 / RPU;
-#pragma unroll
-  for (int i = 0; i < UNITS / 4; ++i) {
-    const int u = wave + 4 * i;
-    const int row = u * RPU + lane / CPR;
-    const int c = (lane % CPR) ^ (VSWZ ? swz_v<D>(row) : swz_k<D>(row));
-    const int key = min(r0 + row, valid - 1);
-    __builtin_amdgcn_global_load_lds((const void*)(src + (int64_t)key * stride + c * 8),
-                                     (LDS void*)(dst + u * 1024), 16, 0, 0);
-  }
-}
+// dword 3 of a raw buffer resource on gfx9: 32-bit data format.  Loads at offsets past
+// the record count return zeros without touching memory.
+constexpr int kBufferFlags = 0x00020000;
+constexpr int kOutOfRange = 0x7ffffff0;   // a byte offset past every record count used here
 
-// 64 rows x rank bf16 of an LR cache into an LDS tile of 64 x 64 bf16 (128-byte rows; the
-// 64-byte halves of rows with bit 1 set are swapped against bank conflicts).  Chunks past
-// the rank are not loaded: the tile is zeroed once, so those columns read as 0.
-__device__ __forceinline__ void load_lr(const bf16* src, int64_t ldl, int rank, int r0, int valid,
-                                        LDS char* dst, int wave, int lane) {
+// Direct buffer->LDS loads of 64-key tiles.  A tile's buffer resource starts at its first
+// key row and covers only the rows inside the key range, so rows past the range (and LR
+// columns past the rank, addressed out of range) land in LDS as zeros; the per-lane byte
+// offsets below are fixed for the whole key loop and each wave writes the 1 KB LDS units
+// u = wave, wave+4, ...  K/V rows are D*2 bytes; LDS slot p of a row holds source chunk
+// p ^ swz(row).  The LR tile is 64 x 64 bf16 (128-byte rows) whose 64-byte halves are
+// swapped on rows with bit 1 set.
+template <int D>
+struct TileLoader {
+  static constexpr int CPR = D / 8;          // 16-byte chunks per K/V row
+  static constexpr int RPU = 64 / CPR;       // rows per 1 KB unit
+  static constexpr int UPW = 64 / RPU / 4;   // units per wave
+  int koff[UPW], voff[UPW], loff[2];
+  __device__ __forceinline__ TileLoader(int wave, int lane, int row_bytes, int l_row_bytes,
+                                        int rank) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int u = wave + 4 * i;
-    const int row = u * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ (((row >> 1) & 1) * 4);
-    if (c * 8 < rank) {
-      const int key = min(r0 + row, valid - 1);
-      __builtin_amdgcn_global_load_lds((const void*)(src + (int64_t)key * ldl + c * 8),
-                                       (LDS void*)(dst + u * 1024), 16, 0, 0);
+    for (int i = 0; i < UPW; ++i) {
+      const int row = (wave + 4 * i) * RPU + lane / CPR;
+      koff[i] = row * row_bytes + (((lane % CPR) ^ swz_k<D>(row)) << 4);
+      voff[i] = row * row_bytes + (((lane % CPR) ^ swz_v<D>(row)) << 4);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int row = (wave + 4 * i) * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ (((row >> 1) & 1) * 4);
+      loff[i] = c * 8 < rank ? row * l_row_bytes + c * 16 : kOutOfRange;
     }
   }
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, int bytes) {
+  // wave-uniform record count: readfirstlane keeps the resource in SGPRs
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0,
+                                           __builtin_amdgcn_readfirstlane(bytes), kBufferFlags);
+}
+
+__device__ __forceinline__ void load_unit(__amdgpu_buffer_rsrc_t r, LDS char* dst, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS void*)dst, 16, voff, 0, 0, 0);
 }
 
 // B operand for key step st (16 keys) from the transposed score/probability block.
@@ -199,13 +206,14 @@ __global__ __launch_bounds__(256, 2) void fla_attn_bf16(const AttnArgs args) {
   int local = w - R.work_start;
   const int rt = local % n_rt;
   local /= n_rt;
-  const int sp = local % n_split;
-  const int g = local / n_split;
+  const int sp = __builtin_amdgcn_readfirstlane(local % n_split);
+  const int g = __builtin_amdgcn_readfirstlane(local / n_split);
   const int G = A->G, Hq = A->Hq, Hkv = A->Hkv;
   const AgentDesc& AG = A->agents[R.agent];
   const int rank = AG.rank;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS bases in M0
   const int col = lane & 31, hi = lane >> 5;
   const int rows_total = Lq * G;
   const int row0 = rt * kTileRows;
@@ -222,8 +230,9 @@ __global__ __launch_bounds__(256, 2) void fla_attn_bf16(const AttnArgs args) {
   const int kmask_from = Lk - Lq + row0 / G + 1;      // first key hidden from some row
   const int n_tiles_req = (Lk + kTileKeys - 1) / kTileKeys;
   const int tps = (n_tiles_req + n_split - 1) / n_split;
-  const int kb = sp * tps * kTileKeys;
-  const int ke = min(min(Lk, kb + tps * kTileKeys), kend_causal);
+  // (wave-uniform; readfirstlane keeps the loop control and buffer resources scalar)
+  const int kb = __builtin_amdgcn_readfirstlane(sp * tps * kTileKeys);
+  const int ke = __builtin_amdgcn_readfirstlane(min(min(Lk, kb + tps * kTileKeys), kend_causal));
   const int n_tiles = ke > kb ? (ke - kb + kTileKeys - 1) / kTileKeys : 0;
   const int mask_from = min(kmask_from, ke);
   // last visible key of this lane's row inside the range, minus its key-lane offset
@@ -253,31 +262,33 @@ __global__ __launch_bounds__(256, 2) void fla_attn_bf16(const AttnArgs args) {
   float m_run = kNegBig, l_run = 0.f;
   const float sl2 = A->scale_log2;
 
-  if (RB) {
-    // LR tiles: columns past the rank are never loaded and must read as zero
-    const f32x4 z = {};
+  const int row_bytes = (int)(kv_stride * 2), l_row_bytes = RB ? (int)(AG.ldl * 2) : 0;
+  const TileLoader<D> ld(wave, lane, row_bytes, l_row_bytes, rank);
+  // tile of 64 keys starting at key k0 into one LDS buffer
+  auto load_tile = [&](int k0, LDS char* dst) {
+    const int rows = max(0, min(ke - k0, kTileKeys));
+    const auto kr = rows_rsrc(Kg + (int64_t)k0 * kv_stride, rows * row_bytes);
+    const auto vr = rows_rsrc(Vg + (int64_t)k0 * kv_stride, rows * row_bytes);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      *(LDS f32x4*)(buf_a + 2 * TILE_KV + tid * 32 + i * 16) = z;
-      *(LDS f32x4*)(buf_b + 2 * TILE_KV + tid * 32 + i * 16) = z;
+    for (int i = 0; i < TileLoader<D>::UPW; ++i) load_unit(kr, dst + (wave + 4 * i) * 1024, ld.koff[i]);
+#pragma unroll
+    for (int i = 0; i < TileLoader<D>::UPW; ++i)
+      load_unit(vr, dst + TILE_KV + (wave + 4 * i) * 1024, ld.voff[i]);
+    if (RB) {
+      // a rank-0 agent's L may be null: its resource covers nothing and reads zeros
+      const auto lr = rows_rsrc(rank > 0 ? (const void*)(Lg + (int64_t)k0 * AG.ldl) : (const void*)Kg,
+                                rank > 0 ? rows * l_row_bytes : 0);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) load_unit(lr, dst + 2 * TILE_KV + (wave + 4 * i) * 1024, ld.loff[i]);
     }
-    __syncthreads();
-  }
-  if (n_tiles > 0) {
-    load_rows<D, false>(Kg, kv_stride, kb, ke, smem, wave, lane);
-    load_rows<D, true>(Vg, kv_stride, kb, ke, smem + TILE_KV, wave, lane);
-    if (RB) load_lr(Lg, AG.ldl, rank, kb, ke, smem + 2 * TILE_KV, wave, lane);
-  }
+  };
+  if (n_tiles > 0) load_tile(kb, smem);
   wait_loads();
   __syncthreads();
 
   auto tile = [&](const int j, const LDS char* cur, LDS char* nxt) {
     const int k0 = kb + j * kTileKeys;
-    if (j + 1 < n_tiles) {
-      load_rows<D, false>(Kg, kv_stride, k0 + kTileKeys, ke, nxt, wave, lane);
-      load_rows<D, true>(Vg, kv_stride, k0 + kTileKeys, ke, nxt + TILE_KV, wave, lane);
-      if (RB) load_lr(Lg, AG.ldl, rank, k0 + kTileKeys, ke, nxt + 2 * TILE_KV, wave, lane);
-    }
+    if (j + 1 < n_tiles) load_tile(k0 + kTileKeys, nxt);
     if (wave_active) {
       // -- Sᵀ = K·Qᵀ for 64 keys (two 32-key blocks)
       f32x16 s[2];
@@ -360,8 +371,12 @@ __global__ __launch_bounds__(256, 2) void fla_attn_bf16(const AttnArgs args) {
     for (int i = 0; i < DB; ++i) accV[i] *= inv;
   }
   if (RB && rank > 0) {   // a rank-0 agent has no B (its pointer may be null)
-    // B_g = B[:, g*D : (g+1)*D] is a "value tile" whose rows are the rank index.
-    load_rows<D, true>((const bf16*)AG.B + g * D, kv_stride, 0, rank, smem + TILE_KV, wave, lane);
+    // B_g = B[:, g*D : (g+1)*D] is a "value tile" whose rows are the rank index; rows
+    // past the rank read as zero
+    const auto br = rows_rsrc((const bf16*)AG.B + g * D, rank * row_bytes);
+#pragma unroll
+    for (int i = 0; i < TileLoader<D>::UPW; ++i)
+      load_unit(br, smem + TILE_KV + (wave + 4 * i) * 1024, ld.voff[i]);
     wait_loads();
     __syncthreads();
     if (wave_active) {

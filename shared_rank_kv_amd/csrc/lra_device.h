@@ -11,7 +11,7 @@ namespace lra {
 __device__ __forceinline__ int find_request(const AttnArgs* A, int w) {
   const int lane = threadIdx.x & 63;
   const int start = lane < A->n_req ? A->reqs[lane].work_start : 0x7fffffff;
-  return __popcll(__ballot(start <= w)) - 1;
+  return __builtin_amdgcn_readfirstlane(__popcll(__ballot(start <= w)) - 1);
 }
 
 // Request that owns combine row `row` (per thread): combine starts are a non-decreasing
