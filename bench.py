@@ -61,26 +61,37 @@ class Flusher:
 
 
 def time_calls(fn, steps, warmup, flush=None):
-    """Per-call durations (ms, HIP events on the current stream) and the total time of the
-    K calls issued back to back (ms; only when no flush is interleaved)."""
+    """Per-call durations (ms) from HIP events on the current stream, and the total (ms).
+
+    Without a flush the K calls run back to back between two events and every call gets
+    total/K: an event recorded between calls costs a cache write-back of its own, which
+    would otherwise be charged to the calls.  With a flush (a kernel that evicts the inputs
+    from the caches between calls), each call is bracketed by its own pair of events and
+    the total is their sum."""
     import torch
     for _ in range(warmup):
-        fn()
-    torch.cuda.synchronize()
-    st, en = _events(steps), _events(steps)
-    t0, t1 = _events(2)
-    t0.record()
-    for i in range(steps):
         if flush is not None:
             flush()
+        fn()
+    torch.cuda.synchronize()
+    if flush is None:
+        t0, t1 = _events(2)
+        t0.record()
+        for _ in range(steps):
+            fn()
+        t1.record()
+        torch.cuda.synchronize()
+        total = t0.elapsed_time(t1)
+        return np.full(steps, total / steps), total
+    st, en = _events(steps), _events(steps)
+    for i in range(steps):
+        flush()
         st[i].record()
         fn()
         en[i].record()
-    t1.record()
     torch.cuda.synchronize()
     per = np.array([s.elapsed_time(e) for s, e in zip(st, en)])
-    total = t0.elapsed_time(t1)
-    return per, total
+    return per, float(per.sum())
 
 
 def roof(achieved, peak, unit, bound, traffic=None):

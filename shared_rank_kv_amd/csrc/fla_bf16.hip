@@ -1,4 +1,4 @@
-// Flash-LoRA-Attention, bf16 storage / fp32 accumulation, for gfx950 (MI355X).
+// Flash-LoRA-Attention prefill, bf16 storage / fp32 accumulation, for gfx950 (MI355X).
 //
 // Computes, per request and query row of agent a (LRAgent summary, section
 // "3. Flash-LoRA-Attention"):
@@ -6,24 +6,23 @@
 // with ONE online softmax shared by both products; L_a stays r wide inside the key loop
 // and B_a is applied once per tile of query rows, after the loop.
 //
-// Workgroup = 4 waves.  It owns one kv head g of one request and a tile of 128
-// (query, head-in-group) rows, row = t*G + h_local, so all q heads that share K/V_base
-// read each LDS tile (GQA-aware).  Each wave owns 32 rows and keeps its scores
-// TRANSPOSED, Sᵀ = K·Qᵀ: with v_mfma_f32_32x32x16_bf16 a lane then holds one query row's
-// scores for 16 keys, the row max/sum need a single cross-half permlane32 swap, and the
-// score accumulator is already laid out as the B operand of the next products
+// A workgroup owns one kv head g of one request and a tile of 256 (query, head-in-group)
+// rows, row = t*G + h_local, so all q heads that share K/V_base read each LDS tile
+// (GQA-aware).  Each of its 8 waves owns 32 rows and keeps its scores TRANSPOSED,
+// Sᵀ = K·Qᵀ: with v_mfma_f32_32x32x16_bf16 a lane then holds one query row's scores for
+// 16 keys, the row max/sum need a single cross-half permlane32 swap, and the score
+// accumulator is already laid out as the B operand of the next products
 // Oᵀ += V_baseᵀ·Pᵀ and (P·L)ᵀ += Lᵀ·Pᵀ (keys are permuted identically on both sides).
-// K, V_base and L tiles of 64 keys stream HBM -> LDS with direct (VGPR-free)
-// global_load_lds_dwordx4, double-buffered, one barrier per tile; K/V rows are
-// XOR-swizzled in 16-byte chunks against LDS bank conflicts.  V_base and L are read
-// with ds_read_b64_tr_b16, which transposes 4x16 blocks inside 16-lane groups, so the
-// caches keep their natural token-major layout in HBM and LDS.
+// K, V_base and L tiles of 64 keys stream HBM -> LDS with direct buffer->LDS loads;
+// K/V rows are XOR-swizzled in 16-byte chunks against LDS bank conflicts.  V_base and L
+// are read with ds_read_b64_tr_b16, which transposes 4x16 blocks inside 16-lane groups,
+// so the caches keep their natural token-major layout in HBM and LDS.
 //
 // When the planner splits a request's key range over several workgroups (to fill the
 // 256 CUs), each applies B to its own partial state (B is linear) and writes
 // (m, l, P·V_base + (P·L)·B) to the workspace; fla_combine_bf16 then merges the splits
-// with their softmax weights.  Decode is the same kernel with one query per request and
-// many key splits.
+// with their softmax weights.  The decode kernel (fla_decode.hip) writes the same partial
+// state and shares the combine pass.
 #include "lra_device.h"
 
 namespace lra {
@@ -65,7 +64,9 @@ __device__ __forceinline__ bf16x8 join(i16x4 lo, i16x4 hi) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
-__device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima, gfx9 encoding); as a
+// builtin the compiler knows the wait happened and places no second one for the same loads
+__device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 __device__ __forceinline__ float lane_bcast(float x, int src) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), src));
@@ -92,28 +93,40 @@ constexpr int kOutOfRange = 0x7ffffff0;   // a byte offset past every record cou
 // u = wave, wave+4, ...  K/V rows are D*2 bytes; LDS slot p of a row holds source chunk
 // p ^ swz(row).  The LR tile is 64 x 64 bf16 (128-byte rows) whose 64-byte halves are
 // swapped on rows with bit 1 set.
-template <int D>
+template <int D, int NW = 4>
 struct TileLoader {
   static constexpr int CPR = D / 8;          // 16-byte chunks per K/V row
   static constexpr int RPU = 64 / CPR;       // rows per 1 KB unit
-  static constexpr int UPW = 64 / RPU / 4;   // units per wave
-  int koff[UPW], voff[UPW], loff[2];
+  static constexpr int UPW = 64 / RPU / NW;  // K (and V) units per wave
+  static constexpr int LPW = 8 / NW;         // LR units per wave
+  int koff[UPW], voff[UPW], loff[LPW];
   __device__ __forceinline__ TileLoader(int wave, int lane, int row_bytes, int l_row_bytes,
                                         int rank) {
 #pragma unroll
     for (int i = 0; i < UPW; ++i) {
-      const int row = (wave + 4 * i) * RPU + lane / CPR;
+      const int row = (wave + NW * i) * RPU + lane / CPR;
       koff[i] = row * row_bytes + (((lane % CPR) ^ swz_k<D>(row)) << 4);
       voff[i] = row * row_bytes + (((lane % CPR) ^ swz_v<D>(row)) << 4);
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int row = (wave + 4 * i) * 8 + (lane >> 3);
+    for (int i = 0; i < LPW; ++i) {
+      const int row = (wave + NW * i) * 8 + (lane >> 3);
       const int c = (lane & 7) ^ (((row >> 1) & 1) * 4);
       loff[i] = c * 8 < rank ? row * l_row_bytes + c * 16 : kOutOfRange;
     }
   }
 };
+
+// Workgroup barrier for LDS operations issued by the waves themselves.  Unlike a
+// workgroup fence it does not wait for direct buffer->LDS loads still in flight (those
+// count in vmcnt): the issuing wave waits for them itself (wait_loads) before the barrier
+// that publishes them.  The empty asm statements keep the compiler from moving memory
+// operations across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, int bytes) {
   // wave-uniform record count: readfirstlane keeps the resource in SGPRs
@@ -178,24 +191,40 @@ __device__ __forceinline__ bf16x8 lfrag(const LDS char* tile, int off, int key0)
 // exactly as well as values below 1.
 constexpr float kRescaleSlack = 8.0f;
 
+// ---------------------------------------------------------------------------------------
+// Prefill kernel, ping-pong schedule (the default prefill path).
+//
+// One 8-wave workgroup per CU; the two halves of the workgroup, A = waves 0-3 and
+// B = waves 4-7, run half a tile apart.  Every SIMD holds
+// one A and one B wave.  Workgroup barriers cut time into phases; in each phase one group
+// issues only matrix work (P·V_base and P·L of the previous tile, then Sᵀ = K·Qᵀ of the
+// current one) while the other runs only the softmax of its current tile, so each SIMD's
+// matrix core and vector ALU are busy at the same time:
+//
+//   phase      0      1      2      3      4     ...
+//   group A   M(0)   V(0)   M(1)   V(1)   M(2)
+//   group B    -     M(0)   V(0)   M(1)   V(1)
+//
+// M(j) = PV(j-1) + S(j), V(j) = softmax(j).  Tile j is read in phases 2j..2j+3, so three
+// LDS buffers rotate; group A issues the direct loads of tile j+1 in phase 2j and they
+// have two phases to complete.  The loop is unrolled by three so that every LDS access
+// names its buffer statically.
 template <int D, int RB>
-__global__ __launch_bounds__(256, 2) void fla_attn_bf16(const AttnArgs args) {
+__global__ __launch_bounds__(512, 1) void fla_prefill_bf16(const AttnArgs args) {
   const AttnArgs* A = (const AttnArgs*)__builtin_amdgcn_kernarg_segment_ptr();
-  constexpr int DB = D / 32;           // 32-row blocks of the transposed output
-  constexpr int KS = D / 16;           // k-steps of the score product
-  constexpr int TILE_KV = 64 * D * 2;  // bytes of one K or V tile
-  constexpr int TILE_L = 64 * 64 * 2;  // bytes of one LR tile (64 x 64 bf16)
-  constexpr int BUF = 2 * TILE_KV + TILE_L;
-  // two statically distinct buffers: with the loop unrolled by two, every LDS read names
-  // the buffer it reads and the compiler can tell it apart from the tile being loaded
-  __shared__ __attribute__((aligned(1024))) char smem_a[BUF];
-  __shared__ __attribute__((aligned(1024))) char smem_b[BUF];
-  LDS char* const buf_a = (LDS char*)smem_a;
-  LDS char* const buf_b = (LDS char*)smem_b;
-  LDS char* smem = buf_a;
+  constexpr int DB = D / 32;
+  constexpr int KS = D / 16;
+  constexpr int TILE_KV = 64 * D * 2;
+  constexpr int TILE_L = 64 * 64 * 2;
+  constexpr int BUF = 2 * TILE_KV + (RB ? TILE_L : 0);
+  constexpr int kRows = kPrefillRows;
+  __shared__ __attribute__((aligned(1024))) char smem0[BUF];
+  __shared__ __attribute__((aligned(1024))) char smem1[BUF];
+  __shared__ __attribute__((aligned(1024))) char smem2[BUF];
+  LDS char* const buf0 = (LDS char*)smem0;
+  LDS char* const buf1 = (LDS char*)smem1;
+  LDS char* const buf2 = (LDS char*)smem2;
 
-  // ---- work item -> (request, kv head, key split, row tile); XCD-major numbering keeps
-  // the row tiles of one (request, kv head, split) on one XCD, sharing its L2.
   const int bid = blockIdx.x;
   const int w = (bid & 7) * A->grid_per_xcd + (bid >> 3);
   if (w >= A->n_work) return;
@@ -204,19 +233,20 @@ __global__ __launch_bounds__(256, 2) void fla_attn_bf16(const AttnArgs args) {
   const int q_start = R.q_start, Lq = R.q_len, k_start = R.k_start, Lk = R.k_len;
   const int n_rt = R.n_rt, n_split = R.n_split;
   int local = w - R.work_start;
-  const int rt = local % n_rt;
+  const int rt = __builtin_amdgcn_readfirstlane(local % n_rt);
   local /= n_rt;
   const int sp = __builtin_amdgcn_readfirstlane(local % n_split);
   const int g = __builtin_amdgcn_readfirstlane(local / n_split);
   const int G = A->G, Hq = A->Hq, Hkv = A->Hkv;
   const AgentDesc& AG = A->agents[R.agent];
-  const int rank = AG.rank;
+  const int rank = RB ? AG.rank : 0;
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS bases in M0
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool group_b = wave >= 4;
   const int col = lane & 31, hi = lane >> 5;
   const int rows_total = Lq * G;
-  const int row0 = rt * kTileRows;
+  const int row0 = rt * kRows;
   const int my_row = row0 + wave * 32 + col;
   const bool valid = my_row < rows_total;
   const int t = valid ? my_row / G : 0;
@@ -224,18 +254,15 @@ __global__ __launch_bounds__(256, 2) void fla_attn_bf16(const AttnArgs args) {
   const int pos = valid ? Lk - Lq + t : Lk - 1;
   const bool wave_active = row0 + wave * 32 < rows_total;
 
-  // key range of this workgroup: its split, cut at the causal end of its last row
-  const int last_row = min(row0 + kTileRows, rows_total) - 1;
+  const int last_row = min(row0 + kRows, rows_total) - 1;
   const int kend_causal = Lk - Lq + last_row / G + 1;
-  const int kmask_from = Lk - Lq + row0 / G + 1;      // first key hidden from some row
+  const int kmask_from = Lk - Lq + row0 / G + 1;
   const int n_tiles_req = (Lk + kTileKeys - 1) / kTileKeys;
   const int tps = (n_tiles_req + n_split - 1) / n_split;
-  // (wave-uniform; readfirstlane keeps the loop control and buffer resources scalar)
   const int kb = __builtin_amdgcn_readfirstlane(sp * tps * kTileKeys);
   const int ke = __builtin_amdgcn_readfirstlane(min(min(Lk, kb + tps * kTileKeys), kend_causal));
   const int n_tiles = ke > kb ? (ke - kb + kTileKeys - 1) / kTileKeys : 0;
   const int mask_from = min(kmask_from, ke);
-  // last visible key of this lane's row inside the range, minus its key-lane offset
   const int vis_last = min(pos, ke - 1) - hi * 4;
 
   const int64_t kv_stride = (int64_t)Hkv * D;
@@ -243,7 +270,6 @@ __global__ __launch_bounds__(256, 2) void fla_attn_bf16(const AttnArgs args) {
   const bf16* Vg = (const bf16*)A->V + ((int64_t)k_start * Hkv + g) * D;
   const bf16* Lg = RB ? (const bf16*)AG.L + (int64_t)k_start * AG.ldl : nullptr;
 
-  // ---- Q fragments (B operand of Sᵀ = K·Qᵀ): lane holds Q[row col][ks*16 + hi*8 .. +7]
   bf16x8 qf[KS];
   {
     const bf16* qrow = (const bf16*)A->Q + ((int64_t)(q_start + t) * Hq + g * G + hl) * D;
@@ -253,6 +279,30 @@ __global__ __launch_bounds__(256, 2) void fla_attn_bf16(const AttnArgs args) {
   }
   const Offsets<D> off(lane);
 
+  const int row_bytes = (int)(kv_stride * 2), l_row_bytes = RB ? (int)(AG.ldl * 2) : 0;
+  // group A (waves 0-3) loads every tile; B never has loads in flight, so no wait the
+  // compiler places for them can stall B's matrix phase
+  const TileLoader<D, 4> ld(wave & 3, lane, row_bytes, l_row_bytes, rank);
+  // this wave's units of the 64-key tile starting at key k0 (group A only)
+  auto load_tile = [&](int k0, LDS char* dst) {
+    const int rows = max(0, min(ke - k0, kTileKeys));
+    const auto kr = rows_rsrc(Kg + (int64_t)k0 * kv_stride, rows * row_bytes);
+    const auto vr = rows_rsrc(Vg + (int64_t)k0 * kv_stride, rows * row_bytes);
+#pragma unroll
+    for (int i = 0; i < TileLoader<D, 4>::UPW; ++i)
+      load_unit(kr, dst + (wave + 4 * i) * 1024, ld.koff[i]);
+#pragma unroll
+    for (int i = 0; i < TileLoader<D, 4>::UPW; ++i)
+      load_unit(vr, dst + TILE_KV + (wave + 4 * i) * 1024, ld.voff[i]);
+    if (RB) {
+      const auto lr = rows_rsrc(rank > 0 ? (const void*)(Lg + (int64_t)k0 * AG.ldl) : (const void*)Kg,
+                                rank > 0 ? rows * l_row_bytes : 0);
+#pragma unroll
+      for (int i = 0; i < TileLoader<D, 4>::LPW; ++i)
+        load_unit(lr, dst + 2 * TILE_KV + (wave + 4 * i) * 1024, ld.loff[i]);
+    }
+  };
+
   f32x16 accV[DB];
   f32x16 accL[RB > 0 ? RB : 1];
 #pragma unroll
@@ -261,133 +311,131 @@ __global__ __launch_bounds__(256, 2) void fla_attn_bf16(const AttnArgs args) {
   for (int i = 0; i < (RB > 0 ? RB : 1); ++i) accL[i] = f32x16{};
   float m_run = kNegBig, l_run = 0.f;
   const float sl2 = A->scale_log2;
+  f32x16 s[2];
+  bf16x8 pf[4];   // P of the previous tile as B operands, 16 keys each
 
-  const int row_bytes = (int)(kv_stride * 2), l_row_bytes = RB ? (int)(AG.ldl * 2) : 0;
-  const TileLoader<D> ld(wave, lane, row_bytes, l_row_bytes, rank);
-  // tile of 64 keys starting at key k0 into one LDS buffer
-  auto load_tile = [&](int k0, LDS char* dst) {
-    const int rows = max(0, min(ke - k0, kTileKeys));
-    const auto kr = rows_rsrc(Kg + (int64_t)k0 * kv_stride, rows * row_bytes);
-    const auto vr = rows_rsrc(Vg + (int64_t)k0 * kv_stride, rows * row_bytes);
+  // matrix phase M(j): PV(j-1) from vbuf, then Sᵀ(j) from kbuf
+  auto mma_phase = [&](int j, const LDS char* kbuf, const LDS char* vbuf) {
+    if (!wave_active) return;
+    if (j >= 1) {
+      const LDS char* vt = vbuf + TILE_KV;
+      const LDS char* lt = vbuf + 2 * TILE_KV;
 #pragma unroll
-    for (int i = 0; i < TileLoader<D>::UPW; ++i) load_unit(kr, dst + (wave + 4 * i) * 1024, ld.koff[i]);
+      for (int st = 0; st < 4; ++st) {
+        const int key0 = (st >> 1) * 32 + (st & 1) * 16;
 #pragma unroll
-    for (int i = 0; i < TileLoader<D>::UPW; ++i)
-      load_unit(vr, dst + TILE_KV + (wave + 4 * i) * 1024, ld.voff[i]);
-    if (RB) {
-      // a rank-0 agent's L may be null: its resource covers nothing and reads zeros
-      const auto lr = rows_rsrc(rank > 0 ? (const void*)(Lg + (int64_t)k0 * AG.ldl) : (const void*)Kg,
-                                rank > 0 ? rows * l_row_bytes : 0);
+        for (int db = 0; db < DB; ++db) accV[db] = mfma32(vfrag<D>(vt, off.v[db], key0), pf[st], accV[db]);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) load_unit(lr, dst + 2 * TILE_KV + (wave + 4 * i) * 1024, ld.loff[i]);
+        for (int rb = 0; rb < RB; ++rb) accL[rb] = mfma32(lfrag(lt, off.l[rb], key0), pf[st], accL[rb]);
+      }
     }
-  };
-  if (n_tiles > 0) load_tile(kb, smem);
-  wait_loads();
-  __syncthreads();
-
-  auto tile = [&](const int j, const LDS char* cur, LDS char* nxt) {
-    const int k0 = kb + j * kTileKeys;
-    if (j + 1 < n_tiles) load_tile(k0 + kTileKeys, nxt);
-    if (wave_active) {
-      // -- Sᵀ = K·Qᵀ for 64 keys (two 32-key blocks)
-      f32x16 s[2];
+    if (j < n_tiles) {
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
         bf16x8 kf[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-          kf[ks] = *(const LDS bf16x8*)(cur + off.k[ks] + kb2 * 32 * (D * 2));
+          kf[ks] = *(const LDS bf16x8*)(kbuf + off.k[ks] + kb2 * 32 * (D * 2));
         s[kb2] = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) s[kb2] = mfma32(kf[ks], qf[ks], s[kb2]);
       }
-      // -- causal mask (only tiles that reach past the first row's last key)
-      if (k0 + kTileKeys > mask_from) {
-        const int lim = vis_last - k0;
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-          for (int e = 0; e < 16; ++e)
-            if (kb2 * 32 + (e >> 2) * 8 + (e & 3) > lim) s[kb2][e] = -INFINITY;
-      }
-      // -- online softmax; the running max moves only when a row max outgrows it by more
-      // than kRescaleSlack, so most tiles skip the accumulator rescale
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-        for (int e = 0; e < 16; e += 2) mx = fmaxf(mx, fmaxf(s[kb2][e], s[kb2][e + 1]));
-      mx = half_max(mx) * sl2;
-      if (__any(mx > m_run + kRescaleSlack)) {
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int i = 0; i < DB; ++i) accV[i] *= alpha;
-#pragma unroll
-        for (int i = 0; i < RB; ++i) accL[i] *= alpha;
-      }
-      float psum = 0.f;
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[kb2][e], sl2, -m_run));
-          s[kb2][e] = p;
-          psum += p;
-        }
-      l_run += psum;
-
-      // -- Oᵀ += V_baseᵀ·Pᵀ and (P·L)ᵀ += Lᵀ·Pᵀ with the same P
-      const LDS char* vt = cur + TILE_KV;
-      const LDS char* lt = cur + 2 * TILE_KV;
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        const bf16x8 pf = pfrag(s[st >> 1], st & 1);
-        const int key0 = (st >> 1) * 32 + (st & 1) * 16;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) accV[db] = mfma32(vfrag<D>(vt, off.v[db], key0), pf, accV[db]);
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) accL[rb] = mfma32(lfrag(lt, off.l[rb], key0), pf, accL[rb]);
-      }
     }
-    wait_loads();
-    __syncthreads();
   };
-  for (int j = 0; j < n_tiles; j += 2) {
-    tile(j, buf_a, buf_b);
-    if (j + 1 < n_tiles) tile(j + 1, buf_b, buf_a);
-  }
+  // vector phase V(j): mask, online softmax, P(j) to bf16 fragments
+  auto valu_phase = [&](int j) {
+    if (!wave_active || j >= n_tiles) return;
+    const int k0 = kb + j * kTileKeys;
+    if (k0 + kTileKeys > mask_from) {
+      const int lim = vis_last - k0;
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (kb2 * 32 + (e >> 2) * 8 + (e & 3) > lim) s[kb2][e] = -INFINITY;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) mx = fmaxf(mx, fmaxf(s[kb2][e], s[kb2][e + 1]));
+    mx = half_max(mx) * sl2;
+    if (__any(mx > m_run + kRescaleSlack)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < DB; ++i) accV[i] *= alpha;
+#pragma unroll
+      for (int i = 0; i < RB; ++i) accL[i] *= alpha;
+    }
+    float psum = 0.f;
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[kb2][e], sl2, -m_run));
+        s[kb2][e] = p;
+        psum += p;
+      }
+    l_run += psum;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) pf[st] = pfrag(s[st >> 1], st & 1);
+  };
+  // one step j of this wave's program (two barriers), buffers named statically.  Group A
+  // issues tile j+1 as it enters M(j) and waits for it after V(j), two phases later.
+  auto step = [&](int j, const LDS char* kbuf, const LDS char* vbuf, LDS char* dma) {
+    if (!group_b && j + 1 < n_tiles) load_tile(kb + (j + 1) * kTileKeys, dma);
+    // the matrix phase runs at raised wave priority so the SIMD's arbiter serves its
+    // MFMA and LDS issue ahead of the partner wave's softmax
+    __builtin_amdgcn_s_setprio(2);
+    mma_phase(j, kbuf, vbuf);
+    __builtin_amdgcn_s_setprio(0);
+    lds_barrier();
+    valu_phase(j);
+    if (!group_b) wait_loads();
+    lds_barrier();
+  };
 
-  const float l_tot = half_sum(l_run);
+  if (!group_b && n_tiles > 0) load_tile(kb, buf0);
+  wait_loads();
+  lds_barrier();
+  if (group_b) lds_barrier();   // B starts one phase late
+  for (int j = 0; j <= n_tiles; j += 3) {
+    step(j, buf0, buf2, buf1);
+    if (j + 1 <= n_tiles) step(j + 1, buf1, buf0, buf2);
+    if (j + 2 <= n_tiles) step(j + 2, buf2, buf1, buf0);
+  }
+  if (!group_b) lds_barrier();   // matches B's extra barrier at the start
+
   // ---- epilogue: acc = P·V_base + (P·L)·B_g with B applied once for the row tile; a
   // whole key range is normalised by l and stored as bf16 O, a key split stores its
   // unnormalised fp32 state (m, l, acc) for fla_combine_bf16.
+  const float l_tot = half_sum(l_run);
   const float inv = n_split == 1 ? 1.f / l_tot : 1.f;
   if (n_split == 1) {
 #pragma unroll
     for (int i = 0; i < DB; ++i) accV[i] *= inv;
   }
-  if (RB && rank > 0) {   // a rank-0 agent has no B (its pointer may be null)
-    // B_g = B[:, g*D : (g+1)*D] is a "value tile" whose rows are the rank index; rows
-    // past the rank read as zero
-    const auto br = rows_rsrc((const bf16*)AG.B + g * D, rank * row_bytes);
+  if (RB && rank > 0) {
+    if (!group_b) {
+      const auto br = rows_rsrc((const bf16*)AG.B + g * D, rank * row_bytes);
 #pragma unroll
-    for (int i = 0; i < TileLoader<D>::UPW; ++i)
-      load_unit(br, smem + TILE_KV + (wave + 4 * i) * 1024, ld.voff[i]);
-    wait_loads();
-    __syncthreads();
+      for (int i = 0; i < TileLoader<D, 4>::UPW; ++i)
+        load_unit(br, buf0 + TILE_KV + (wave + 4 * i) * 1024, ld.voff[i]);
+      wait_loads();
+    }
+    lds_barrier();
     if (wave_active) {
       const int nst = (rank + 15) / 16;
       for (int st = 0; st < nst; ++st) {
         const f32x16 lsc = accL[(RB > 1) ? (st >> 1) : 0] * inv;
-        const bf16x8 pf = pfrag(lsc, st & 1);
+        const bf16x8 p2 = pfrag(lsc, st & 1);
         const int key0 = (st >> 1) * 32 + (st & 1) * 16;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
-          accV[db] = mfma32(vfrag<D>(smem + TILE_KV, off.v[db], key0), pf, accV[db]);
+          accV[db] = mfma32(vfrag<D>(buf0 + TILE_KV, off.v[db], key0), p2, accV[db]);
       }
     }
   }
@@ -474,11 +522,11 @@ __global__ __launch_bounds__(256) void fla_combine_bf16(const AttnArgs args) {
 
 }  // namespace
 
-hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, int max_rank, int n_grid,
-                            hipStream_t s) {
+hipError_t launch_prefill_bf16(const AttnArgs& a, int head_dim, int max_rank, int n_grid,
+                               hipStream_t s) {
   const int rb = max_rank > 32 ? 2 : (max_rank > 0 ? 1 : 0);
 #define LRA_LAUNCH(D, RB) \
-  hipLaunchKernelGGL((fla_attn_bf16<D, RB>), dim3(n_grid), dim3(kThreads), 0, s, a)
+  hipLaunchKernelGGL((fla_prefill_bf16<D, RB>), dim3(n_grid), dim3(512), 0, s, a)
   if (head_dim == 128) {
     if (rb == 0) LRA_LAUNCH(128, 0);
     else if (rb == 1) LRA_LAUNCH(128, 1);

@@ -184,7 +184,7 @@ Plan make_plan(const AttnShape& s, bool decode, const int32_t* q_len, const int3
   int64_t total_wg = 0;
   for (size_t i = 0; i < n; ++i) {
     const int ql = decode ? 1 : q_len[p.active[i]];
-    p.n_rt[i] = (int)ceil_div((int64_t)ql * G, lra::kTileRows);
+    p.n_rt[i] = (int)ceil_div((int64_t)ql * G, decode ? lra::kTileRows : lra::kPrefillRows);
     total_wg += (int64_t)s.Hkv * p.n_rt[i];
   }
   if (decode) {
@@ -195,7 +195,8 @@ Plan make_plan(const AttnShape& s, bool decode, const int32_t* q_len, const int3
       p.n_split[i] = (int)std::max<int64_t>(1, std::min<int64_t>({ceil_div(kl, chunk), tiles, 64}));
     }
   } else {
-    const int target = env_int("LRA_PREFILL_TARGET_WG", 512);
+    // one workgroup per CU: split keys until the launch covers the 256 CUs
+    const int target = env_int("LRA_PREFILL_TARGET_WG", 256);
     if (total_wg < target) {
       const int64_t factor = ceil_div(target, std::max<int64_t>(total_wg, 1));
       for (size_t i = 0; i < n; ++i) {
@@ -283,7 +284,7 @@ int run_attention(const AttnShape& s, bool decode, const Requests& rq, const voi
       int max_rank = 0;
       for (size_t i = c0; i < c1; ++i) max_rank = std::max(max_rank, ad.ranks[rq.agent[p.active[i]]]);
       e = decode ? lra::launch_decode_bf16(a, s.D, max_rank, grid, stream)
-                 : lra::launch_attn_bf16(a, s.D, max_rank, grid, stream);
+                 : lra::launch_prefill_bf16(a, s.D, max_rank, grid, stream);
       if (e == hipSuccess && comb > 0) e = lra::launch_combine_bf16(a, s.D, stream);
     } else {
       a.grid_per_xcd = 0;

@@ -17,6 +17,7 @@ constexpr int kReqsPerLaunch = 64;   // larger batches are split into several la
 // Tile geometry of the bf16 attention kernel (see fla_bf16.hip).
 constexpr int kTileRows = 128;       // (query, head-in-group) rows per workgroup
 constexpr int kTileKeys = 64;        // keys per LDS tile
+constexpr int kPrefillRows = 256;    // rows per workgroup of the ping-pong prefill kernel
 constexpr int kThreads = 256;        // 4 waves of 64
 
 struct AgentDesc {
@@ -72,8 +73,8 @@ struct PrecomputeArgs {
 };
 
 // Launchers (return the HIP status of the launch).
-hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, int max_rank, int n_grid,
-                            hipStream_t s);
+hipError_t launch_prefill_bf16(const AttnArgs& a, int head_dim, int max_rank, int n_grid,
+                               hipStream_t s);
 hipError_t launch_decode_bf16(const AttnArgs& a, int head_dim, int max_rank, int n_grid,
                               hipStream_t s);
 hipError_t launch_combine_bf16(const AttnArgs& a, int head_dim, hipStream_t s);
