@@ -29,6 +29,7 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int KC = 64;          // d_model chunk
 constexpr int TM = 128;         // rows per workgroup
+constexpr int PF = 2;           // chunks in flight in registers ahead of the LDS tiles
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -59,7 +60,7 @@ __global__ __launch_bounds__(256, 1) void lr_precompute_bf16(const PrecomputeArg
   const int64_t T = P->T, ldx = P->ldx, lda = P->lda;
   const int R = P->R;
   const int nk = (int)(P->d_model / KC);       // d_model % 64 == 0 (checked by the host)
-  const int nk_pad = (nk + 1) / 2 * 2;         // padded chunks meet zero rows of A_cat
+  const int nk_pad = (nk + PF - 1) / PF * PF;   // padded chunks meet zero rows of A_cat
   const int64_t row0 = (int64_t)blockIdx.x * TM;
 
   // X chunk (128 rows x 128 bytes): each lane loads 16-byte units, 8 whole rows per wave
@@ -80,7 +81,7 @@ __global__ __launch_bounds__(256, 1) void lr_precompute_bf16(const PrecomputeArg
   // the same 128-byte column of the 8 KB rows at once.
   const int rot = (int)(blockIdx.x % nk);
   auto chunk = [&](int kc) { return kc < nk ? (kc + rot) % nk : nk - 1; };
-  u32x4 xr[2][UX];
+  u32x4 xr[PF][UX];
   auto load_x = [&](u32x4 (&dst)[UX], int kc) {
     const int64_t koff = (int64_t)chunk(kc) * KC * 2;
 #pragma unroll
@@ -101,7 +102,7 @@ __global__ __launch_bounds__(256, 1) void lr_precompute_bf16(const PrecomputeArg
   }
   // A_cat tile (64 d_model rows x NBT*32 columns), staged through registers into a padded
   // LDS tile; columns past R and padded chunks are stored as zeros.
-  u32x4 areg[2][CPT];
+  u32x4 areg[PF][CPT];
   uint32_t aoff[CPT];
   int a_ok[CPT], lds_off[CPT];
 #pragma unroll
@@ -136,21 +137,25 @@ __global__ __launch_bounds__(256, 1) void lr_precompute_bf16(const PrecomputeArg
 #pragma unroll
     for (int nb = 0; nb < NBW; ++nb) acc[mb][nb] = f32x16{};
 
-  load_a(areg[0], 0);
-  load_x(xr[0], 0);
-  load_a(areg[1], 1);
-  load_x(xr[1], 1);
+#pragma unroll
+  for (int i = 0; i < PF; ++i) {
+    load_a(areg[i], i);
+    load_x(xr[i], i);
+  }
   store_a(areg[0], 0, 0);
   store_x(xr[0], 0);
   __syncthreads();
 
-  for (int kc0 = 0; kc0 < nk_pad; kc0 += 2) {
+  // Chunk c travels global -> register slot c % PF (issued in iteration c - PF) -> LDS
+  // (stored at the end of iteration c - 1) -> MFMA operands (iteration c).  The loop is
+  // unrolled by PF so every slot index is static and the wait counts are exact.
+  for (int kc0 = 0; kc0 < nk_pad; kc0 += PF) {
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
+    for (int st = 0; st < PF; ++st) {
       const int kc = kc0 + st;
-      // both operands two chunks ahead, into the register slots freed last iteration
-      load_a(areg[st & 1], kc + 2);
-      load_x(xr[st & 1], kc + 2);
+      // slot st held chunk kc, already in LDS: refill it with chunk kc + PF
+      load_a(areg[st], kc + PF);
+      load_x(xr[st], kc + PF);
       const LDS char* xt = xlds + (kc % XS) * XTILE;
       const LDS char* at = alds + (kc & 1) * ATILE;
 #pragma unroll
@@ -169,8 +174,8 @@ __global__ __launch_bounds__(256, 1) void lr_precompute_bf16(const PrecomputeArg
 #pragma unroll
           for (int nb = 0; nb < NBW; ++nb) acc[mb][nb] = mfma32(af[mb], bf[nb], acc[mb][nb]);
       }
-      store_a(areg[(st + 1) & 1], (kc + 1) & 1, kc + 1);
-      store_x(xr[(st + 1) & 1], kc + 1);
+      store_a(areg[(st + 1) % PF], (kc + 1) & 1, kc + 1);
+      store_x(xr[(st + 1) % PF], kc + 1);
       __syncthreads();
     }
   }
