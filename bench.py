@@ -24,6 +24,7 @@ before timing starts.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import platform
@@ -94,6 +95,39 @@ def time_calls(fn, steps, warmup, flush=None):
     return per, float(per.sum())
 
 
+# HBM bytes per call measured with rocprofv3 FETCH_SIZE and WRITE_SIZE (each calibrated by
+# what the same counter reads for a plain 1 GiB device copy); the per-kernel summaries and
+# the commands are under profiles/.  The figures describe the kernels built from sources
+# with this digest and are reported as null for any other sources.
+TRAFFIC_SOURCES_SHA256 = "f7db8801cdc001d9dee457080c95fed2bc6c524bd2e1eba96c56ff63cd147eba"
+TRAFFIC_BYTES = {
+    "llama8b-prefill-1024q-9216k-r16": 125963823,
+    "decode-64x16384-r16": 4419852757,
+    "lr-precompute-32768x4096-3x64": 386046420,
+    "longctx-prefill-512q-32768k-r64": 245354596,
+}
+
+
+def sources_sha256():
+    """Digest of the C ABI header and every source liblra.so is built from."""
+    here = os.path.dirname(os.path.abspath(__file__))
+    csrc = os.path.join(here, "shared_rank_kv_amd", "csrc")
+    files = [os.path.join(here, "include", "lra.h")] + sorted(
+        os.path.join(csrc, f) for f in os.listdir(csrc) if f.endswith((".hip", ".h", ".cpp")))
+    h = hashlib.sha256()
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic_bytes(workload):
+    if sources_sha256() != TRAFFIC_SOURCES_SHA256:
+        return None
+    return TRAFFIC_BYTES.get(workload)
+
+
 def roof(achieved, peak, unit, bound, traffic=None):
     return {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
             "frac": round(achieved / peak, 4), "traffic": traffic}
@@ -159,7 +193,7 @@ def bench_decode(steps, warmup, flush):
     gbs = nbytes / (ms * 1e-3) / 1e9
     return {"workload": prob.name, "value": round(gbs, 1), "unit": "GB/s",
             "ms_per_call": round(ms, 4), "bytes": nbytes, "flop": flop,
-            "roofline": roof(gbs, accounting.PEAK_HBM_GBS, "GB/s", "hbm")}
+            "roofline": roof(gbs, accounting.PEAK_HBM_GBS, "GB/s", "hbm", traffic_bytes(prob.name))}
 
 
 def bench_longctx(steps, warmup, flush):
@@ -178,7 +212,8 @@ def bench_longctx(steps, warmup, flush):
     precompute = {"workload": pre.name, "value": round(pgbs, 1), "unit": "GB/s",
                   "tflops": round(pflop / (pms * 1e-3) / 1e12, 1), "ms_per_call": round(pms, 4),
                   "bytes": pbytes, "flop": pflop,
-                  "roofline": roof(pgbs, accounting.PEAK_HBM_GBS, "GB/s", "hbm")}
+                  "roofline": roof(pgbs, accounting.PEAK_HBM_GBS, "GB/s", "hbm",
+                                   traffic_bytes(pre.name))}
     del X, pfn
     prob = workloads.longctx_prefill(agents=(0,))
     _, dev = upload(prob, L=Ls)
@@ -189,7 +224,8 @@ def bench_longctx(steps, warmup, flush):
     tf = flop / (ms * 1e-3) / 1e12
     longctx = {"workload": prob.name, "value": round(tf, 1), "unit": "TFLOP/s",
                "ms_per_call": round(ms, 4), "flop": flop, "bytes": nbytes,
-               "roofline": roof(tf, accounting.PEAK_BF16_TFLOPS, "TFLOP/s", "mfma")}
+               "roofline": roof(tf, accounting.PEAK_BF16_TFLOPS, "TFLOP/s", "mfma",
+                                traffic_bytes(prob.name))}
     return precompute, longctx
 
 
@@ -321,7 +357,8 @@ def main():
         "config": {"workload": prob.name, "q_len": 1024, "k_len": 9216, "q_heads": 32,
                    "kv_heads": 8, "head_dim": 128, "rank": 16, "agents": 3, "timed_agent": 0,
                    "flop_per_step": r["flop"], "bytes_per_step": r["bytes"]},
-        "roofline": roof(achieved, accounting.PEAK_BF16_TFLOPS, "TFLOP/s", "mfma"),
+        "roofline": roof(achieved, accounting.PEAK_BF16_TFLOPS, "TFLOP/s", "mfma",
+                         traffic_bytes(prob.name)),
         "roofline_kernel": "lra_attn_prefill call (attention kernel, plus the combine pass "
                            "when the planner splits keys)",
     }
