@@ -191,6 +191,9 @@ __device__ __forceinline__ bf16x8 lfrag(const LDS char* tile, int off, int key0)
 // exactly as well as values below 1.
 constexpr float kRescaleSlack = 8.0f;
 
+// LDS reads the prefill matrix phase issues before the first MFMA of its P·V part
+constexpr int kPfReads = 18;
+
 // ---------------------------------------------------------------------------------------
 // Prefill kernel, ping-pong schedule (the default prefill path).
 //
@@ -328,18 +331,37 @@ __global__ __launch_bounds__(512, 1) void fla_prefill_bf16(const AttnArgs args) 
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) accL[rb] = mfma32(lfrag(lt, off.l[rb], key0), pf[st], accL[rb]);
       }
+      // scheduling: kPfReads LDS reads first, then one MFMA per two further reads, so each
+      // MFMA's operands were requested several MFMAs earlier (the compiler's own order kept
+      // only one fragment in flight and the MFMAs waited on LDS latency)
+      constexpr int NR = 8 * DB + 8 * RB, NM = 4 * DB + 4 * RB;   // LDS reads, MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, kPfReads, 0);
+#pragma unroll
+      for (int i = 0; i < (NR - kPfReads) / 2; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, NM - (NR - kPfReads) / 2, 0);
     }
     if (j < n_tiles) {
+      // the two 32-key blocks alternate, so consecutive MFMAs are independent
+      s[0] = f32x16{};
+      s[1] = f32x16{};
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2) {
-        bf16x8 kf[KS];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          kf[ks] = *(const LDS bf16x8*)(kbuf + off.k[ks] + kb2 * 32 * (D * 2));
-        s[kb2] = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) s[kb2] = mfma32(kf[ks], qf[ks], s[kb2]);
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 k0f = *(const LDS bf16x8*)(kbuf + off.k[ks]);
+        const bf16x8 k1f = *(const LDS bf16x8*)(kbuf + off.k[ks] + 32 * (D * 2));
+        s[0] = mfma32(k0f, qf[ks], s[0]);
+        s[1] = mfma32(k1f, qf[ks], s[1]);
       }
+      // (the same pattern for the score part: 8 reads ahead)
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int i = 0; i < KS - 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, KS + 4, 0);
     }
   };
   // vector phase V(j): mask, online softmax, P(j) to bf16 fragments
