@@ -209,8 +209,8 @@ constexpr int kPfReads = 18;
 //   group B    -     M(0)   V(0)   M(1)   V(1)
 //
 // M(j) = PV(j-1) + S(j), V(j) = softmax(j).  Tile j is read in phases 2j..2j+3, so three
-// LDS buffers rotate; group A issues the direct loads of tile j+1 in phase 2j and they
-// have two phases to complete.  The loop is unrolled by three so that every LDS access
+// LDS buffers rotate; group B issues the direct loads of tile j+1 in phase 2j (its softmax
+// phase) and they have two phases to complete.  The loop is unrolled by three so that every LDS access
 // names its buffer statically.
 template <int D, int RB>
 __global__ __launch_bounds__(512, 1) void fla_prefill_bf16(const AttnArgs args) {
@@ -283,26 +283,25 @@ __global__ __launch_bounds__(512, 1) void fla_prefill_bf16(const AttnArgs args) 
   const Offsets<D> off(lane);
 
   const int row_bytes = (int)(kv_stride * 2), l_row_bytes = RB ? (int)(AG.ldl * 2) : 0;
-  // group A (waves 0-3) loads every tile; B never has loads in flight, so no wait the
-  // compiler places for them can stall B's matrix phase
+  // group B (waves 4-7) loads every tile
   const TileLoader<D, 4> ld(wave & 3, lane, row_bytes, l_row_bytes, rank);
-  // this wave's units of the 64-key tile starting at key k0 (group A only)
+  // this wave's units of the 64-key tile starting at key k0 (group B only)
   auto load_tile = [&](int k0, LDS char* dst) {
     const int rows = max(0, min(ke - k0, kTileKeys));
     const auto kr = rows_rsrc(Kg + (int64_t)k0 * kv_stride, rows * row_bytes);
     const auto vr = rows_rsrc(Vg + (int64_t)k0 * kv_stride, rows * row_bytes);
 #pragma unroll
     for (int i = 0; i < TileLoader<D, 4>::UPW; ++i)
-      load_unit(kr, dst + (wave + 4 * i) * 1024, ld.koff[i]);
+      load_unit(kr, dst + ((wave & 3) + 4 * i) * 1024, ld.koff[i]);
 #pragma unroll
     for (int i = 0; i < TileLoader<D, 4>::UPW; ++i)
-      load_unit(vr, dst + TILE_KV + (wave + 4 * i) * 1024, ld.voff[i]);
+      load_unit(vr, dst + TILE_KV + ((wave & 3) + 4 * i) * 1024, ld.voff[i]);
     if (RB) {
       const auto lr = rows_rsrc(rank > 0 ? (const void*)(Lg + (int64_t)k0 * AG.ldl) : (const void*)Kg,
                                 rank > 0 ? rows * l_row_bytes : 0);
 #pragma unroll
       for (int i = 0; i < TileLoader<D, 4>::LPW; ++i)
-        load_unit(lr, dst + 2 * TILE_KV + (wave + 4 * i) * 1024, ld.loff[i]);
+        load_unit(lr, dst + 2 * TILE_KV + ((wave & 3) + 4 * i) * 1024, ld.loff[i]);
     }
   };
 
@@ -405,29 +404,34 @@ __global__ __launch_bounds__(512, 1) void fla_prefill_bf16(const AttnArgs args) 
 #pragma unroll
     for (int st = 0; st < 4; ++st) pf[st] = pfrag(s[st >> 1], st & 1);
   };
-  // one step j of this wave's program (two barriers), buffers named statically.  Group A
-  // issues tile j+1 as it enters M(j) and waits for it after V(j), two phases later.
+  // one step j of this wave's program (two barriers), buffers named statically.  Group B
+  // issues the loads of tile j+2 as it enters V(j) (global phase 2j+2, while group A runs
+  // its matrix phase) and waits for them after M(j+1), two phases later; group A never has
+  // loads in flight, so nothing delays the start of its matrix phase.
   auto step = [&](int j, const LDS char* kbuf, const LDS char* vbuf, LDS char* dma) {
-    if (!group_b && j + 1 < n_tiles) load_tile(kb + (j + 1) * kTileKeys, dma);
     // the matrix phase runs at raised wave priority so the SIMD's arbiter serves its
     // MFMA and LDS issue ahead of the partner wave's softmax
     __builtin_amdgcn_s_setprio(2);
     mma_phase(j, kbuf, vbuf);
     __builtin_amdgcn_s_setprio(0);
+    if (group_b) wait_loads();
     lds_barrier();
+    if (group_b && j + 2 < n_tiles) load_tile(kb + (j + 2) * kTileKeys, dma);
     valu_phase(j);
-    if (!group_b) wait_loads();
     lds_barrier();
   };
 
-  if (!group_b && n_tiles > 0) load_tile(kb, buf0);
+  if (group_b && n_tiles > 0) load_tile(kb, buf0);
   wait_loads();
   lds_barrier();
-  if (group_b) lds_barrier();   // B starts one phase late
+  if (group_b) {               // B starts one phase late; tile 1 is issued in that phase
+    if (n_tiles > 1) load_tile(kb + kTileKeys, buf1);
+    lds_barrier();
+  }
   for (int j = 0; j <= n_tiles; j += 3) {
-    step(j, buf0, buf2, buf1);
-    if (j + 1 <= n_tiles) step(j + 1, buf1, buf0, buf2);
-    if (j + 2 <= n_tiles) step(j + 2, buf2, buf1, buf0);
+    step(j, buf0, buf2, buf2);
+    if (j + 1 <= n_tiles) step(j + 1, buf1, buf0, buf0);
+    if (j + 2 <= n_tiles) step(j + 2, buf2, buf1, buf1);
   }
   if (!group_b) lds_barrier();   // matches B's extra barrier at the start
 
@@ -441,11 +445,11 @@ __global__ __launch_bounds__(512, 1) void fla_prefill_bf16(const AttnArgs args) 
     for (int i = 0; i < DB; ++i) accV[i] *= inv;
   }
   if (RB && rank > 0) {
-    if (!group_b) {
+    if (group_b) {
       const auto br = rows_rsrc((const bf16*)AG.B + g * D, rank * row_bytes);
 #pragma unroll
       for (int i = 0; i < TileLoader<D, 4>::UPW; ++i)
-        load_unit(br, buf0 + TILE_KV + (wave + 4 * i) * 1024, ld.voff[i]);
+        load_unit(br, buf0 + TILE_KV + ((wave & 3) + 4 * i) * 1024, ld.voff[i]);
       wait_loads();
     }
     lds_barrier();
