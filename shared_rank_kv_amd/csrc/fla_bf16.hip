@@ -271,7 +271,8 @@ __global__ __launch_bounds__(512, 1) void fla_prefill_bf16(const AttnArgs args) 
   const int64_t kv_stride = (int64_t)Hkv * D;
   const bf16* Kg = (const bf16*)A->K + ((int64_t)k_start * Hkv + g) * D;
   const bf16* Vg = (const bf16*)A->V + ((int64_t)k_start * Hkv + g) * D;
-  const bf16* Lg = RB ? (const bf16*)AG.L + (int64_t)k_start * AG.ldl : nullptr;
+  const int64_t ldl = RB ? AG.ldl : 0;   // read once: kernel-argument loads in the loop stall
+  const bf16* Lg = RB ? (const bf16*)AG.L + (int64_t)k_start * ldl : nullptr;
 
   bf16x8 qf[KS];
   {
@@ -282,12 +283,12 @@ __global__ __launch_bounds__(512, 1) void fla_prefill_bf16(const AttnArgs args) 
   }
   const Offsets<D> off(lane);
 
-  const int row_bytes = (int)(kv_stride * 2), l_row_bytes = RB ? (int)(AG.ldl * 2) : 0;
+  const int row_bytes = (int)(kv_stride * 2), l_row_bytes = (int)(ldl * 2);
   // group B (waves 4-7) loads every tile
   const TileLoader<D, 4> ld(wave & 3, lane, row_bytes, l_row_bytes, rank);
   // this wave's units of the 64-key tile starting at key k0 (group B only)
   auto load_tile = [&](int k0, LDS char* dst) {
-    const int rows = max(0, min(ke - k0, kTileKeys));
+    const int rows = __builtin_amdgcn_readfirstlane(max(0, min(ke - k0, kTileKeys)));
     const auto kr = rows_rsrc(Kg + (int64_t)k0 * kv_stride, rows * row_bytes);
     const auto vr = rows_rsrc(Vg + (int64_t)k0 * kv_stride, rows * row_bytes);
 #pragma unroll
@@ -297,7 +298,7 @@ __global__ __launch_bounds__(512, 1) void fla_prefill_bf16(const AttnArgs args) 
     for (int i = 0; i < TileLoader<D, 4>::UPW; ++i)
       load_unit(vr, dst + TILE_KV + ((wave & 3) + 4 * i) * 1024, ld.voff[i]);
     if (RB) {
-      const auto lr = rows_rsrc(rank > 0 ? (const void*)(Lg + (int64_t)k0 * AG.ldl) : (const void*)Kg,
+      const auto lr = rows_rsrc(rank > 0 ? (const void*)(Lg + (int64_t)k0 * ldl) : (const void*)Kg,
                                 rank > 0 ? rows * l_row_bytes : 0);
 #pragma unroll
       for (int i = 0; i < TileLoader<D, 4>::LPW; ++i)
