@@ -67,6 +67,12 @@ __device__ __forceinline__ bf16x8 join(i16x4 lo, i16x4 hi) {
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima, gfx9 encoding); as a
 // builtin the compiler knows the wait happened and places no second one for the same loads
 __device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt vmcnt(N): all but the N most recently issued vector-memory loads are done
+template <int N>
+__device__ __forceinline__ void wait_loads_but() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
 
 __device__ __forceinline__ float lane_bcast(float x, int src) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), src));
@@ -209,8 +215,8 @@ constexpr int kPfReads = 18;
 //   group B    -     M(0)   V(0)   M(1)   V(1)
 //
 // M(j) = PV(j-1) + S(j), V(j) = softmax(j).  Tile j is read in phases 2j..2j+3, so three
-// LDS buffers rotate; group B issues the direct loads of tile j+1 in phase 2j (its softmax
-// phase) and they have two phases to complete.  The loop is unrolled by three so that every LDS access
+// LDS buffers rotate.  Each group issues part of the direct loads in its softmax phase:
+// group A the K rows, group B the V_base and L rows (see step).  The loop is unrolled by three so that every LDS access
 // names its buffer statically.
 template <int D, int RB>
 __global__ __launch_bounds__(512, 1) void fla_prefill_bf16(const AttnArgs args) {
@@ -284,16 +290,22 @@ __global__ __launch_bounds__(512, 1) void fla_prefill_bf16(const AttnArgs args) 
   const Offsets<D> off(lane);
 
   const int row_bytes = (int)(kv_stride * 2), l_row_bytes = (int)(ldl * 2);
-  // group B (waves 4-7) loads every tile
+  // tile loads are split by part: group A (waves 0-3) loads K, group B (waves 4-7) loads
+  // V_base and L, each during its own softmax phase (see step below)
   const TileLoader<D, 4> ld(wave & 3, lane, row_bytes, l_row_bytes, rank);
-  // this wave's units of the 64-key tile starting at key k0 (group B only)
-  auto load_tile = [&](int k0, LDS char* dst) {
-    const int rows = __builtin_amdgcn_readfirstlane(max(0, min(ke - k0, kTileKeys)));
-    const auto kr = rows_rsrc(Kg + (int64_t)k0 * kv_stride, rows * row_bytes);
-    const auto vr = rows_rsrc(Vg + (int64_t)k0 * kv_stride, rows * row_bytes);
+  constexpr int N_K = TileLoader<D, 4>::UPW;                       // K loads per A wave
+  constexpr int N_V = TileLoader<D, 4>::UPW + (RB ? TileLoader<D, 4>::LPW : 0);   // per B wave
+  auto tile_rows = [&](int k0) {
+    return __builtin_amdgcn_readfirstlane(max(0, min(ke - k0, kTileKeys)));
+  };
+  auto load_k = [&](int k0, LDS char* dst) {   // this A wave's units of K rows k0..k0+63
+    const auto kr = rows_rsrc(Kg + (int64_t)k0 * kv_stride, tile_rows(k0) * row_bytes);
 #pragma unroll
-    for (int i = 0; i < TileLoader<D, 4>::UPW; ++i)
-      load_unit(kr, dst + ((wave & 3) + 4 * i) * 1024, ld.koff[i]);
+    for (int i = 0; i < N_K; ++i) load_unit(kr, dst + ((wave & 3) + 4 * i) * 1024, ld.koff[i]);
+  };
+  auto load_vl = [&](int k0, LDS char* dst) {  // this B wave's units of V_base and L rows
+    const int rows = tile_rows(k0);
+    const auto vr = rows_rsrc(Vg + (int64_t)k0 * kv_stride, rows * row_bytes);
 #pragma unroll
     for (int i = 0; i < TileLoader<D, 4>::UPW; ++i)
       load_unit(vr, dst + TILE_KV + ((wave & 3) + 4 * i) * 1024, ld.voff[i]);
@@ -405,28 +417,49 @@ __global__ __launch_bounds__(512, 1) void fla_prefill_bf16(const AttnArgs args) 
 #pragma unroll
     for (int st = 0; st < 4; ++st) pf[st] = pfrag(s[st >> 1], st & 1);
   };
-  // one step j of this wave's program (two barriers), buffers named statically.  Group B
-  // issues the loads of tile j+2 as it enters V(j) (global phase 2j+2, while group A runs
-  // its matrix phase) and waits for them after M(j+1), two phases later; group A never has
-  // loads in flight, so nothing delays the start of its matrix phase.
+  // one step j of this wave's program (two barriers), buffers named statically.
+  //  - K(t) is read in phases 2t and 2t+1; group A issues it as it enters V(t-2) (phase
+  //    2t-3) and waits for it at the end of V(t-1): three phases of latency.
+  //  - V_base(t) and L(t) are read in phases 2t+2 and 2t+3; group B issues them as it
+  //    enters V(t-2) (phase 2t-2) and waits for them at the end of M(t): four phases.
+  // Each wait leaves the next tile's loads in flight (vmcnt(N)), except where no next tile
+  // was issued.  With the parts split, both softmax phases carry a share of the issue work.
   auto step = [&](int j, const LDS char* kbuf, const LDS char* vbuf, LDS char* dma) {
     // the matrix phase runs at raised wave priority so the SIMD's arbiter serves its
     // MFMA and LDS issue ahead of the partner wave's softmax
     __builtin_amdgcn_s_setprio(2);
     mma_phase(j, kbuf, vbuf);
     __builtin_amdgcn_s_setprio(0);
-    if (group_b) wait_loads();
+    if (group_b) {                       // V(j) complete; V(j+1) may stay in flight
+      if (j + 1 < n_tiles) wait_loads_but<N_V>();
+      else wait_loads();
+    }
     lds_barrier();
-    if (group_b && j + 2 < n_tiles) load_tile(kb + (j + 2) * kTileKeys, dma);
+    if (j + 2 < n_tiles) {
+      if (group_b) load_vl(kb + (j + 2) * kTileKeys, dma);
+      else load_k(kb + (j + 2) * kTileKeys, dma);
+    }
     valu_phase(j);
+    if (!group_b) {                      // K(j+1) complete; K(j+2) may stay in flight
+      if (j + 2 < n_tiles) wait_loads_but<N_K>();
+      else wait_loads();
+    }
     lds_barrier();
   };
 
-  if (group_b && n_tiles > 0) load_tile(kb, buf0);
-  wait_loads();
+  // prologue: K(0), K(1) and V(0) before phase 0; B issues V(1) in its extra phase 0
+  if (!group_b) {
+    if (n_tiles > 0) load_k(kb, buf0);
+    if (n_tiles > 1) load_k(kb + kTileKeys, buf1);
+    if (n_tiles > 1) wait_loads_but<N_K>();
+    else wait_loads();
+  } else {
+    if (n_tiles > 0) load_vl(kb, buf0);
+    wait_loads();
+  }
   lds_barrier();
-  if (group_b) {               // B starts one phase late; tile 1 is issued in that phase
-    if (n_tiles > 1) load_tile(kb + kTileKeys, buf1);
+  if (group_b) {               // B starts one phase late
+    if (n_tiles > 1) load_vl(kb + kTileKeys, buf1);
     lds_barrier();
   }
   for (int j = 0; j <= n_tiles; j += 3) {
@@ -446,6 +479,7 @@ __global__ __launch_bounds__(512, 1) void fla_prefill_bf16(const AttnArgs args) 
     for (int i = 0; i < DB; ++i) accV[i] *= inv;
   }
   if (RB && rank > 0) {
+    wait_loads();                 // nothing of the key loop is still in flight
     if (group_b) {
       const auto br = rows_rsrc((const bf16*)AG.B + g * D, rank * row_bytes);
 #pragma unroll
