@@ -192,7 +192,8 @@ def bench_decode(steps, warmup, flush):
     ms = float(np.median(per))
     gbs = nbytes / (ms * 1e-3) / 1e9
     return {"workload": prob.name, "value": round(gbs, 1), "unit": "GB/s",
-            "ms_per_call": round(ms, 4), "bytes": nbytes, "flop": flop,
+            "ms_per_call": round(ms, 4), "ms_min": round(float(per.min()), 4),
+            "ms_max": round(float(per.max()), 4), "bytes": nbytes, "flop": flop,
             "roofline": roof(gbs, accounting.PEAK_HBM_GBS, "GB/s", "hbm", traffic_bytes(prob.name))}
 
 
@@ -211,6 +212,7 @@ def bench_longctx(steps, warmup, flush):
     pgbs = pbytes / (pms * 1e-3) / 1e9
     precompute = {"workload": pre.name, "value": round(pgbs, 1), "unit": "GB/s",
                   "tflops": round(pflop / (pms * 1e-3) / 1e12, 1), "ms_per_call": round(pms, 4),
+                  "ms_min": round(float(per.min()), 4), "ms_max": round(float(per.max()), 4),
                   "bytes": pbytes, "flop": pflop,
                   "roofline": roof(pgbs, accounting.PEAK_HBM_GBS, "GB/s", "hbm",
                                    traffic_bytes(pre.name))}
@@ -235,6 +237,7 @@ def bench_mixed(steps, warmup):
     layers = []
     t = time.time()
     tflop = tbytes = 0
+    req_ms = 0.0
     for layer in range(workloads.MIXED_LAYERS):
         prob = workloads.mixed_batch_layer(layer)
         _, dev = upload(prob)
@@ -243,6 +246,10 @@ def bench_mixed(steps, warmup):
         f, b = accounting.attention_work(prob)
         tflop += f
         tbytes += b
+        # per-request bound: each request on its own at whichever roofline binds it
+        req_ms += sum(max(fr / (accounting.PEAK_BF16_TFLOPS * 1e12),
+                          br / (accounting.PEAK_HBM_GBS * 1e9))
+                      for fr, br in accounting.attention_work_per_request(prob)) * 1e3
         layers.append((prob, dev))
     log(f"[bench] mixed-batch inputs (32 layers) ready in {time.time() - t:.1f}s")
 
@@ -262,7 +269,9 @@ def bench_mixed(steps, warmup):
     torch.cuda.empty_cache()
     return {"workload": "mixed32-32req-ranks8-16-32-64", "ms_per_32_layers": round(ms, 3),
             "flop": tflop, "bytes": tbytes, "tflops": round(tflop / (ms * 1e-3) / 1e12, 1),
-            "roofline_ms": round(ideal_ms, 3), "frac_of_roofline": round(ideal_ms / ms, 4)}
+            "roofline_ms": round(ideal_ms, 3), "frac_of_roofline": round(ideal_ms / ms, 4),
+            "per_request_roofline_ms": round(req_ms, 3),
+            "frac_of_per_request_roofline": round(req_ms / ms, 4)}
 
 
 def cpu_baseline(prob, cpu, target_s=10.0):
@@ -300,6 +309,47 @@ def cpu_baseline(prob, cpu, target_s=10.0):
             "kind": "oracle", "seconds": round(t, 2),
             "sample": f"{prob.name}, agent 0, query rows 0..{n - 1} of {lq}, all {Hq} q heads, "
                       f"fp64 numpy/BLAS on {platform.processor() or platform.machine()}"}
+
+
+def ceilings(steps, warmup):
+    """Attainable rates on this GPU, for context only (not targets): a 512 MiB streaming
+    read (torch reduction), a 1 GiB device copy, and torch.matmul in bf16 at 8192^3."""
+    import torch
+    buf = torch.ones(64 << 20, dtype=torch.int64, device="cuda")
+    per, _ = time_calls(lambda: buf.sum(), steps, warmup)
+    read = buf.numel() * 8 / float(np.median(per)) / 1e6
+    del buf
+    src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    per, _ = time_calls(lambda: dst.copy_(src), steps, warmup)
+    copy = 2 * (1 << 30) / float(np.median(per)) / 1e6
+    del src, dst
+    n = 8192
+    a = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+    b = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+    per, _ = time_calls(lambda: torch.matmul(a, b), max(5, steps // 2), warmup)
+    mm = 2 * n ** 3 / float(np.median(per)) / 1e9
+    del a, b
+    torch.cuda.empty_cache()
+    return {"read_GBps": round(read, 1), "copy_GBps": round(copy, 1),
+            "torch_matmul_bf16_8192_TFLOPs": round(mm, 1), "note": "context only"}
+
+
+def environment():
+    import subprocess
+    import torch
+    props = torch.cuda.get_device_properties(0)
+    env = {"device": props.name, "compute_units": props.multi_processor_count,
+           "torch": torch.__version__, "hip": torch.version.hip}
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True,
+                           text=True, timeout=20)
+        clk = json.loads(r.stdout)
+        card = next(iter(clk.values()))
+        env["clocks"] = {k: v for k, v in card.items() if k.lower().startswith(("sclk", "mclk"))}
+    except Exception:  # noqa: BLE001
+        env["clocks"] = None
+    return env
 
 
 def run_only(args):
@@ -377,6 +427,9 @@ def main():
         if args.mixed:
             log("[bench] mixed 32-layer batch")
             out["mixed"] = bench_mixed(args.steps, args.warmup)
+        log("[bench] ceilings")
+        out["ceilings"] = ceilings(args.steps, args.warmup)
+        out["env"] = environment()
     print(json.dumps(out), flush=True)
 
 

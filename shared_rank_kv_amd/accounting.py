@@ -56,6 +56,24 @@ def attention_work(prob):
     return flop, kv_bytes + l_bytes + b_bytes + qo_bytes
 
 
+def attention_work_per_request(prob):
+    """[(flop, bytes)] of each request on its own: its K/V rows, its LR rows, its agent's
+    B, its Q and O.  For requests with disjoint key rows the sums equal attention_work."""
+    e = _elem(prob.dtype)
+    D, Hq, Hkv = prob.head_dim, prob.n_q_heads, prob.n_kv_heads
+    out = []
+    for b in range(prob.batch):
+        lq, lk = int(prob.q_len[b]), int(prob.k_len[b])
+        if lq == 0:
+            continue
+        r = prob.ranks[int(prob.agent_idx[b])]
+        pairs = lq * (lk - lq) + lq * (lq + 1) // 2
+        flop = Hq * pairs * (4 * D + 2 * r) + Hq * lq * 2 * r * D
+        nbytes = lk * Hkv * D * e * 2 + lk * r * e + r * Hkv * D * e + lq * Hq * D * e * 2
+        out.append((flop, nbytes))
+    return out
+
+
 def precompute_work(p):
     e = _elem(p.dtype)
     R = sum(p.ranks)
