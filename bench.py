@@ -99,12 +99,12 @@ def time_calls(fn, steps, warmup, flush=None):
 # what the same counter reads for a plain 1 GiB device copy); the per-kernel summaries and
 # the commands are under profiles/.  The figures describe the kernels built from sources
 # with this digest and are reported as null for any other sources.
-TRAFFIC_SOURCES_SHA256 = "82919f64e57208008a168f4e3109ee6e1c994919d8c15d76288c71cbfbdc84f4"
+TRAFFIC_SOURCES_SHA256 = "557589b0c892eb3ad6383ee95dcb6464ecd8f300ef6644c4b47720efc2b02ec6"
 TRAFFIC_BYTES = {
-    "llama8b-prefill-1024q-9216k-r16": 127035711,
-    "decode-64x16384-r16": 4418305877,
-    "lr-precompute-32768x4096-3x64": 386041246,
-    "longctx-prefill-512q-32768k-r64": 245419404,
+    "llama8b-prefill-1024q-9216k-r16": 127035520,
+    "decode-64x16384-r16": 4418271946,
+    "lr-precompute-32768x4096-3x64": 293965514,
+    "longctx-prefill-512q-32768k-r64": 245419210,
 }
 
 

@@ -405,6 +405,10 @@ int lra_precompute_lr(int dtype, int64_t T, int64_t d_model, const void* X, int6
   if (dtype == LRA_DTYPE_BF16 && (lda % 8 != 0))
     return fail(LRA_ERR_INVALID, "lda %lld must be a multiple of 8 for bf16", (long long)lda);
   if (R > 256) return fail(LRA_ERR_UNSUPPORTED, "sum of ranks %lld > 256", (long long)R);
+  // the bf16 kernel addresses 64 rows of X, or a 64-row chunk of A_cat, with 32-bit offsets
+  if (dtype == LRA_DTYPE_BF16 && (ldx >= (1 << 24) || lda >= (1 << 24)))
+    return fail(LRA_ERR_UNSUPPORTED, "bf16 ldx %lld / lda %lld must be below 2^24",
+                (long long)ldx, (long long)lda);
   lra::PrecomputeArgs a;
   std::memset(&a, 0, sizeof(a));
   a.X = X;

@@ -4,13 +4,16 @@
 //
 // bf16 path: a tall-skinny GEMM L_cat[T, R] = X[T, d_model]·A_cat[d_model, R] with
 // R = sum of ranks <= 256.  The work is bound by reading X once from HBM (R = 192 gives
-// ~180 FLOP per byte, under the MI355X ridge), so every workgroup owns 128 rows of X and
-// ALL R columns, reading X from HBM exactly once.  X chunks (128 rows x 64 d_model values,
-// whole 128-byte row segments per 8-lane group) and A_cat chunks (64 x R) are loaded two
-// chunks ahead into registers and stored into LDS tiles (X swizzled, A_cat padded); the
-// B operands are read with ds_read_b64_tr_b16.  Four waves split the 128 x R tile 2 x 2 (64 rows x R/2 columns
-// each) with v_mfma_f32_32x32x16_bf16; the epilogue rounds to bf16 and scatters column
-// blocks to each agent's L_a.
+// ~180 FLOP per byte, under the MI355X ridge).  The kernel computes the transposed tile
+// L_catᵀ = A_catᵀ·Xᵀ with v_mfma_f32_16x16x32_bf16, so that X is the B operand: in that
+// operand a lane holds eight consecutive d_model values of one token, which is 16
+// contiguous bytes of an X row.  X therefore streams from HBM straight into MFMA operand
+// registers and never touches LDS; it is fetched in visits of four 64-value chunks (512
+// contiguous bytes of each row), one visit ahead.  A_cat (small, L2-resident) is the A
+// operand: it travels by direct buffer->LDS loads into a ring of four LDS tiles, three
+// chunks ahead, and is read back with the transposing LDS read.  Each workgroup owns 128
+// tokens and all R columns, so X is read from HBM exactly once; the epilogue rounds to
+// bf16 and scatters column blocks to each agent's L_a.
 //
 // fp32 path: a plain LDS-tiled fp32 GEMM (exactness, not throughput).
 #include "lra_internal.h"
@@ -19,20 +22,22 @@ namespace lra {
 namespace {
 
 typedef __bf16 bf16;
+typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 #define LDS __attribute__((address_space(3)))
 
-constexpr int KC = 64;          // d_model chunk
-constexpr int TM = 128;         // rows per workgroup
-constexpr int PF = 2;           // chunks in flight in registers ahead of the LDS tiles
+constexpr int KC = 64;                        // d_model values per chunk
+constexpr int TM = 128;                       // tokens per workgroup
+constexpr int kBufferFlags = 0x00020000;      // raw buffer resource, dword format
+constexpr int kOutOfRange = 0x7ffffff0;       // a buffer offset past every record count
 
-__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ bf16x8 join(i16x4 lo, i16x4 hi) {
@@ -40,163 +45,227 @@ __device__ __forceinline__ bf16x8 join(i16x4 lo, i16x4 hi) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
-template <int NBW>
+__device__ __forceinline__ i16x4 tr_read(const LDS char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS i16x4*)p);
+}
+
+// s_waitcnt vmcnt(N): all but the N most recently issued vector-memory operations are done
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// Barrier for LDS data: waits for this wave's own LDS operations only (direct
+// buffer->LDS loads are waited for with wait_vm by the wave that issued them).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// 16-byte buffer load into registers (zero past the resource's record count)
+__device__ __forceinline__ u32x4 load_b128(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+// 16-byte direct buffer->LDS load: lane l's bytes land at dst + 16 l
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, LDS char* dst, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LDS void*)dst, 16, voff, 0, 0, 0);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0,
+                                           __builtin_amdgcn_readfirstlane(bytes), kBufferFlags);
+}
+
+// Row k of an A_cat chunk sits in LDS row a_row(k).  Inside each 32-row block the bits of
+// k = 8g + 4h + e become 16h + 4g + e: the two transposing reads of lane group g (LDS rows
+// 4g + e, then 16 + 4g + e, e = 0..3) then return A_cat rows 8g .. 8g + 7, the same eight
+// consecutive d_model values that the lane holds of its X row.  a_k inverts it.
+__device__ __forceinline__ int a_k(int rho) {
+  return (rho & ~31) | (((rho >> 2) & 3) << 3) | (((rho >> 4) & 1) << 2) | (rho & 3);
+}
+
+// 16-byte unit p of LDS tile row rho holds A_cat unit p ^ a_swz(rho).  The transposing read
+// of a lane group fetches rows 4g + e (e = 0..3) x 32 bytes; a quarter-wave (one g) must
+// fall on distinct 32-byte slots of a 128-byte bank cycle and a half-wave (g and g + 1) on
+// distinct slots of a 256-byte cycle.  Rows of 256 or 512 bytes all start at bank 0: the
+// swizzle takes eight slots (an involution inside aligned groups of 16 units).  Rows of 128
+// or 384 bytes alternate between the halves of the 256-byte cycle: four slots per row
+// parity, permuted with g so that rows 4g + e and 4(g + 1) + e differ (groups of 8 units).
+// Row offsets that are multiples of 16 (the second read, later k-steps) leave it unchanged.
+template <int NCB>
+__device__ __forceinline__ int a_swz(int rho) {
+  return NCB % 8 == 0 ? 2 * (rho & 7) : 2 * ((rho & 3) ^ ((rho >> 2) & 1));
+}
+
+// NCB: 16-column blocks of A_cat (R padded up to 64, 128, 192 or 256 columns).
+template <int NCB>
 __global__ __launch_bounds__(256, 1) void lr_precompute_bf16(const PrecomputeArgs args) {
   const PrecomputeArgs* P = (const PrecomputeArgs*)__builtin_amdgcn_kernarg_segment_ptr();
-  constexpr int NBT = 2 * NBW;                 // 32-column blocks in the padded A_cat tile
-  constexpr int RS = NBT * 32 * 2 + 16;        // A_cat LDS row stride (bytes), padded
-  constexpr int CPT = NBT;                     // 16-byte A_cat chunks per thread per tile
-  constexpr int XS = 2;                        // X LDS stages
-  constexpr int XTILE = TM * KC * 2;           // 16 KB: 128 rows x 64 d_model values
-  constexpr int UX = XTILE / 1024 / 4;         // X direct loads per wave per chunk (4)
-  constexpr int ATILE = KC * RS;
-  __shared__ __attribute__((aligned(1024))) char smem_raw[XS * XTILE + 2 * ATILE];
-  LDS char* xlds = (LDS char*)smem_raw;
-  LDS char* alds = xlds + XS * XTILE;
+  constexpr int RB = NCB * 32;                 // bytes per LDS tile row (NCB * 16 columns)
+  constexpr int ATILE = KC * RB;               // bytes per A_cat chunk tile
+  constexpr int NAW = ATILE / 1024 / 4;        // 1 KB direct loads per wave per chunk
+  constexpr int NB = 2;                        // 16-token blocks per wave (32 tokens)
+  constexpr int MB = NCB;                      // 16-column blocks (all of R)
+  constexpr int XN = NB * 2;                   // X loads per wave per chunk (2 k-steps)
+  constexpr int XV = 4;                        // chunks per X visit (512 bytes of each row)
+  constexpr int NT = 4;                        // A_cat tiles in the LDS ring
+  constexpr int UNROLL = 2 * XV;               // chunk steps per loop pass (two X visits)
+  static_assert(NAW * 4 * 1024 == ATILE, "tile split over four waves");
+  static_assert(UNROLL % NT == 0, "static tile indices");
+  // A_cat ring: chunk kc lives in tile kc % NT.  Separate arrays let the compiler see that
+  // the tile being filled by direct loads is not the one being read.
+  __shared__ __attribute__((aligned(1024))) char sa0[ATILE];
+  __shared__ __attribute__((aligned(1024))) char sa1[ATILE];
+  __shared__ __attribute__((aligned(1024))) char sa2[ATILE];
+  __shared__ __attribute__((aligned(1024))) char sa3[ATILE];
+  LDS char* const tiles[NT] = {(LDS char*)sa0, (LDS char*)sa1, (LDS char*)sa2, (LDS char*)sa3};
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int wm = wave & 1, wn = wave >> 1;
-  const int hi = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: base pointers stay scalar
+  const int grp = lane >> 4, col = lane & 15;
   const int64_t T = P->T, ldx = P->ldx, lda = P->lda;
   const int R = P->R;
   const int nk = (int)(P->d_model / KC);       // d_model % 64 == 0 (checked by the host)
-  const int nk_pad = (nk + PF - 1) / PF * PF;   // padded chunks meet zero rows of A_cat
-  const int64_t row0 = (int64_t)blockIdx.x * TM;
+  const int nk_pad = (nk + UNROLL - 1) / UNROLL * UNROLL;   // padded chunks read zeros
+  const int64_t t0 = (int64_t)blockIdx.x * TM + wave * 16 * NB;   // first token of this wave
 
-  // X chunk (128 rows x 128 bytes): each lane loads 16-byte units, 8 whole rows per wave
-  // instruction, two chunks ahead into registers, and stores them into an LDS tile where
-  // unit p of row r holds global unit p ^ ((r >> 1) & 7); that makes the operand reads
-  // below (32 consecutive rows at one unit) bank-conflict free.  Rows past T repeat row T-1
-  // (their results are never stored).  (Register staging measured faster here than direct
-  // global->LDS loads.)
-  const char* xsrc[UX];
+  // X operand (token block nb, k-step ks of a chunk): lane (grp, col) holds d_model values
+  // 32 ks + 8 grp .. + 8 of the chunk, of token t0 + 16 nb + col.  Tokens past T read zeros
+  // (their results are not stored); chunks past d_model read zeros through an empty
+  // resource.
+  const int64_t left = T - t0;
+  const int x_rows = left <= 0 ? 0 : (left < 16 * NB ? (int)left : 16 * NB);
+  const __amdgpu_buffer_rsrc_t x_rsrc =
+      make_rsrc((const char*)P->X + t0 * ldx * 2, (int)(x_rows * ldx * 2));
+  const __amdgpu_buffer_rsrc_t none = make_rsrc(P->X, 0);
+  int xoff[NB];
 #pragma unroll
-  for (int i = 0; i < UX; ++i) {
-    const int u = wave + 4 * i;
-    const int row = u * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ ((row >> 1) & 7);
-    xsrc[i] = (const char*)P->X + (min(row0 + row, T - 1) * ldx + c * 8) * 2;
-  }
-  // Workgroups start their d_model sweep at different chunks so that they do not all read
-  // the same 128-byte column of the 8 KB rows at once.
-  const int rot = (int)(blockIdx.x % nk);
-  auto chunk = [&](int kc) { return kc < nk ? (kc + rot) % nk : nk - 1; };
-  u32x4 xr[PF][UX];
-  auto load_x = [&](u32x4 (&dst)[UX], int kc) {
-    const int64_t koff = (int64_t)chunk(kc) * KC * 2;
+  for (int nb = 0; nb < NB; ++nb) xoff[nb] = (int)((nb * 16 + col) * ldx * 2) + grp * 16;
+  // The workgroups of one XCD sweep d_model in the same order, so each A_cat chunk is read
+  // into that XCD's L2 once and serves all of them; the eight XCDs start eight visits apart.
+  const int rot = (int)(blockIdx.x & 7) * (nk >> 3) & ~(XV - 1);
+  auto chunk = [&](int kc) { return kc < nk ? (kc + rot < nk ? kc + rot : kc + rot - nk) : 0; };
+  u32x4 xop[UNROLL][NB][2];
+  auto load_x = [&](u32x4 (&dst)[NB][2], int kc) {
+    __amdgpu_buffer_rsrc_t r = none;
+    if (kc < nk) r = x_rsrc;
+    const int soff = chunk(kc) * KC * 2;
 #pragma unroll
-    for (int i = 0; i < UX; ++i) dst[i] = *(const u32x4*)(xsrc[i] + koff);
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) dst[nb][ks] = load_b128(r, xoff[nb] + ks * 64, soff);
   };
-  auto store_x = [&](const u32x4 (&src)[UX], int kc) {
-    LDS char* dst = xlds + (kc % XS) * XTILE;
+
+  // A_cat chunk -> LDS tile: the 1 KB unit i of this wave covers tile units
+  // (wave * NAW + i) * 64 + lane; columns past R read zeros.
+  int aoff_g[NAW];
 #pragma unroll
-    for (int i = 0; i < UX; ++i) *(LDS u32x4*)(dst + (wave + 4 * i) * 1024 + lane * 16) = src[i];
-  };
-  // A operand (row lane&31 of m-block mb, d_model values ks*16 + hi*8 ..) from the X tile
-  int xoff[2][4];
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
-    const int row = wm * 64 + mb * 32 + (lane & 31);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) xoff[mb][ks] = row * 128 + (((2 * ks + hi) ^ ((row >> 1) & 7)) << 4);
-  }
-  // A_cat tile (64 d_model rows x NBT*32 columns), staged through registers into a padded
-  // LDS tile; columns past R and padded chunks are stored as zeros.
-  u32x4 areg[PF][CPT];
-  uint32_t aoff[CPT];
-  int a_ok[CPT], lds_off[CPT];
-#pragma unroll
-  for (int i = 0; i < CPT; ++i) {
-    const int ch = tid + 256 * i;
-    const int k = ch / (NBT * 4), c = ch % (NBT * 4);
-    a_ok[i] = c * 8 < R;
-    aoff[i] = (uint32_t)((k * lda + min(c, R / 8 - 1) * 8) * 2);
-    lds_off[i] = k * RS + c * 16;
+  for (int i = 0; i < NAW; ++i) {
+    const int u = (wave * NAW + i) * 64 + lane;
+    const int rho = u / (2 * NCB), c = (u % (2 * NCB)) ^ a_swz<NCB>(rho);
+    aoff_g[i] = c * 8 < R ? (int)((a_k(rho) * lda + c * 8) * 2) : kOutOfRange;
   }
   const char* Abase = (const char*)P->A;
-  auto load_a = [&](u32x4 (&dst)[CPT], int kc) {
-    const char* base = Abase + (int64_t)chunk(kc) * KC * lda * 2;
+  const int a_bytes = (int)(KC * lda * 2);
+  auto load_a = [&](LDS char* tile, int kc) {
+    const __amdgpu_buffer_rsrc_t r =
+        make_rsrc(Abase + (int64_t)chunk(kc) * KC * lda * 2, kc < nk ? a_bytes : 0);
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) dst[i] = *(const u32x4*)(base + aoff[i]);
+    for (int i = 0; i < NAW; ++i)
+      load_lds16(r, tile + (wave * NAW + i) * 1024, aoff_g[i]);
   };
-  auto store_a = [&](const u32x4 (&src)[CPT], int buf, int kc) {
-    const bool chunk_ok = kc < nk;
-#pragma unroll
-    for (int i = 0; i < CPT; ++i)
-      *(LDS u32x4*)(alds + buf * ATILE + lds_off[i]) = (chunk_ok && a_ok[i]) ? src[i] : u32x4{};
-  };
-  const int g16 = lane >> 4, jj = lane & 15;
-  int boff[NBW];
-#pragma unroll
-  for (int nb = 0; nb < NBW; ++nb)
-    boff[nb] = ((g16 >> 1) * 8 + (jj >> 2)) * RS + ((wn * NBW + nb) * 32 + (g16 & 1) * 16 + (jj & 3) * 4) * 2;
 
-  f32x16 acc[2][NBW];
+  // A operand (column block cb, k-step ks): lane (grp, e = col / 4, q = col % 4) points the
+  // transposing read at LDS row 32 ks + 4 grp + e (then + 16), columns 16 cb + 4 q .. + 4;
+  // the read hands lane (grp, col) column 16 cb + col.
+  int aoff[MB];
+  {
+    const int e = col >> 2, q = col & 3;
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < NBW; ++nb) acc[mb][nb] = f32x16{};
-
-#pragma unroll
-  for (int i = 0; i < PF; ++i) {
-    load_a(areg[i], i);
-    load_x(xr[i], i);
+    for (int cb = 0; cb < MB; ++cb)
+      aoff[cb] = (4 * grp + e) * RB + ((2 * cb + (q >> 1)) ^ a_swz<NCB>(4 * grp + e)) * 16 +
+                 (q & 1) * 8;
   }
-  store_a(areg[0], 0, 0);
-  store_x(xr[0], 0);
-  __syncthreads();
 
-  // Chunk c travels global -> register slot c % PF (issued in iteration c - PF) -> LDS
-  // (stored at the end of iteration c - 1) -> MFMA operands (iteration c).  The loop is
-  // unrolled by PF so every slot index is static and the wait counts are exact.
-  for (int kc0 = 0; kc0 < nk_pad; kc0 += PF) {
+  f32x4 acc[NB][MB];
 #pragma unroll
-    for (int st = 0; st < PF; ++st) {
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int cb = 0; cb < MB; ++cb) acc[nb][cb] = f32x4{};
+
+  // Issue order per chunk step kc, before its MFMAs: A_cat chunk kc + 3 (into the tile chunk
+  // kc - 1 used), then, on every fourth step, the X visit of chunks kc + 4 .. kc + 7.  At the end of step
+  // kc the tile of chunk kc + 1 must be complete: issued two steps earlier, it was followed
+  // by two more tiles and, unless kc % 4 == 3, by one X visit, all of which may stay in
+  // flight.  The prologue issues the same sequence for the virtual steps -4 .. -1.
+#pragma unroll
+  for (int i = 0; i < XV; ++i) load_x(xop[i], i);
+#pragma unroll
+  for (int i = 0; i < NT - 1; ++i) load_a(tiles[i], i);
+  wait_vm<2 * NAW>();
+  lds_barrier();
+
+  for (int kc0 = 0; kc0 < nk_pad; kc0 += UNROLL) {
+#pragma unroll
+    for (int st = 0; st < UNROLL; ++st) {
       const int kc = kc0 + st;
-      // slot st held chunk kc, already in LDS: refill it with chunk kc + PF
-      load_a(areg[st], kc + PF);
-      load_x(xr[st], kc + PF);
-      const LDS char* xt = xlds + (kc % XS) * XTILE;
-      const LDS char* at = alds + (kc & 1) * ATILE;
+      const LDS char* at = tiles[st % NT];
+      // loads first, so that they are in flight during this step's MFMAs: the tile of chunk
+      // kc - 1 and the X slots of chunks kc - 4 .. kc - 1 are free (the barrier that ended
+      // step kc - 1 follows every read of them)
+      load_a(tiles[(st + NT - 1) % NT], kc + NT - 1);
+      if (st % XV == 0) {
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        bf16x8 af[2], bf[NBW];
+        for (int i = 0; i < XV; ++i) load_x(xop[(st + XV + i) % UNROLL], kc + XV + i);
+      }
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) af[mb] = *(const LDS bf16x8*)(xt + xoff[mb][ks]);
+      for (int ks = 0; ks < 2; ++ks) {
+        bf16x8 aop[MB];
 #pragma unroll
-        for (int nb = 0; nb < NBW; ++nb) {
-          const LDS char* p = at + boff[nb] + ks * 16 * RS;
-          bf[nb] = join(__builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS i16x4*)p),
-                        __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS i16x4*)(p + 4 * RS)));
+        for (int cb = 0; cb < MB; ++cb) {
+          const LDS char* p = at + aoff[cb] + ks * 32 * RB;
+          aop[cb] = join(tr_read(p), tr_read(p + 16 * RB));
         }
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+        for (int cb = 0; cb < MB; ++cb)
 #pragma unroll
-          for (int nb = 0; nb < NBW; ++nb) acc[mb][nb] = mfma32(af[mb], bf[nb], acc[mb][nb]);
+          for (int nb = 0; nb < NB; ++nb)
+            acc[nb][cb] = mfma16(aop[cb], __builtin_bit_cast(bf16x8, xop[st][nb][ks]),
+                                 acc[nb][cb]);
       }
-      store_a(areg[(st + 1) % PF], (kc + 1) & 1, kc + 1);
-      store_x(xr[(st + 1) % PF], kc + 1);
-      __syncthreads();
+      if (st % XV == XV - 1) wait_vm<2 * NAW>();
+      else wait_vm<2 * NAW + XV * XN>();
+      lds_barrier();
     }
   }
 
-  // epilogue: round to bf16 and scatter columns to their agent's LR cache
+  // epilogue: acc[nb][cb] register j of lane (grp, col) is column 16 gcb + 4 grp + j of
+  // token t0 + 16 nb + col.  Ranks are multiples of 8, so those four columns belong to one
+  // agent; they are stored as one 8-byte write where that agent's layout allows it.
 #pragma unroll
-  for (int nb = 0; nb < NBW; ++nb) {
-    const int colg = (wn * NBW + nb) * 32 + (lane & 31);
-    if (colg >= R) continue;
+  for (int cb = 0; cb < MB; ++cb) {
+    const int c0 = cb * 16 + 4 * grp;
+    if (c0 >= R) continue;
     int a = 0;
-    while (a + 1 < P->n_agents && P->col_start[a + 1] <= colg) ++a;
-    bf16* Lp = (bf16*)P->Lout[a];
+    while (a + 1 < P->n_agents && P->col_start[a + 1] <= c0) ++a;
+    bf16* Lp = (bf16*)P->Lout[a] + (c0 - P->col_start[a]);
     const int64_t ld = P->ldl[a];
-    const int c = colg - P->col_start[a];
+    const bool vec = ((uintptr_t)Lp & 7) == 0 && (ld & 3) == 0;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int nb = 0; nb < NB; ++nb) {
+      const int64_t t = t0 + nb * 16 + col;
+      if (t >= T) continue;
+      const f32x4 v = acc[nb][cb];
+      if (vec) {
+        *(bf16x4*)(Lp + t * ld) = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+      } else {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int64_t r = row0 + wm * 64 + mb * 32 + (e >> 2) * 8 + hi * 4 + (e & 3);
-        if (r < T) Lp[r * ld + c] = (bf16)acc[mb][nb][e];
+        for (int j = 0; j < 4; ++j) Lp[t * ld + j] = (bf16)v[j];
       }
+    }
   }
 }
 
@@ -248,14 +317,15 @@ __global__ __launch_bounds__(256) void lr_precompute_f32(const PrecomputeArgs ar
 
 hipError_t launch_precompute_bf16(const PrecomputeArgs& a, hipStream_t s) {
   const int tiles = (int)((a.T + TM - 1) / TM);
-  const int nbt = (a.R + 31) / 32;
-  const int nbw = (nbt + 1) / 2;
-  switch (nbw) {
-    case 1: hipLaunchKernelGGL(lr_precompute_bf16<1>, dim3(tiles), dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL(lr_precompute_bf16<2>, dim3(tiles), dim3(256), 0, s, a); break;
-    case 3: hipLaunchKernelGGL(lr_precompute_bf16<3>, dim3(tiles), dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL(lr_precompute_bf16<4>, dim3(tiles), dim3(256), 0, s, a); break;
+#define LRA_LAUNCH(NCB) \
+  hipLaunchKernelGGL((lr_precompute_bf16<NCB>), dim3(tiles), dim3(256), 0, s, a)
+  switch ((a.R + 63) / 64) {              // 64-column groups of A_cat
+    case 1: LRA_LAUNCH(4); break;
+    case 2: LRA_LAUNCH(8); break;
+    case 3: LRA_LAUNCH(12); break;
+    default: LRA_LAUNCH(16); break;
   }
+#undef LRA_LAUNCH
   return hipGetLastError();
 }
 

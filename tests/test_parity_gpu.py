@@ -182,6 +182,11 @@ def test_bf16_decode_shapes(shape, chunk, monkeypatch):
 @pytest.mark.parametrize("dtype,T,dm,ranks", [("bf16", 300, 256, (8, 16, 64)),
                                               ("bf16", 1000, 512, (64, 64, 64)),
                                               ("bf16", 129, 4096, (32,)),
+                                              # d_model chunks not a multiple of the
+                                              # prefetch depth; widest and narrowest R
+                                              ("bf16", 517, 320, (64, 64, 64, 64)),
+                                              ("bf16", 64, 1344, (8,)),
+                                              ("bf16", 255, 192, (0, 40, 24)),
                                               ("f32", 77, 136, (8, 24))])
 def test_precompute(dtype, T, dm, ranks):
     import oracle
@@ -215,3 +220,19 @@ def test_precompute_into_column_blocks_of_one_buffer():
     lra.lra_precompute_lr(X.cuda(), A_cat, (16, 32), sep)
     torch.cuda.synchronize()
     assert torch.equal(buf[:, :16], sep[0]) and torch.equal(buf[:, 16:], sep[1])
+
+
+def test_precompute_into_rows_of_odd_stride():
+    # rows of 50 elements (a stride that is not a multiple of 4): the epilogue cannot use
+    # 8-byte stores; the results must not change
+    from shared_rank_kv_amd import lra
+    p = workloads.PrecomputeProblem("pre-odd", "bf16", 333, 512, (16, 32), seed=711)
+    X, A = p.X(), [p.A(0), p.A(1)]
+    A_cat = torch.cat(A, 1).contiguous().cuda()
+    buf = torch.zeros(333, 50, dtype=torch.bfloat16, device="cuda")
+    lra.lra_precompute_lr(X.cuda(), A_cat, (16, 32), [buf[:, 2:18], buf[:, 18:50]])
+    sep = [torch.zeros(333, r, dtype=torch.bfloat16, device="cuda") for r in (16, 32)]
+    lra.lra_precompute_lr(X.cuda(), A_cat, (16, 32), sep)
+    torch.cuda.synchronize()
+    assert torch.equal(buf[:, 2:18], sep[0]) and torch.equal(buf[:, 18:50], sep[1])
+    assert (buf[:, :2] == 0).all()
