@@ -12,6 +12,9 @@ back to back between device synchronisations.
 Also reported, each timed on its own (HIP events around every call, the 256 MB MALL
 flushed between calls of the HBM-bound ones):
   decode      64 requests x 16384 keys, one query each, rank 16, 4 agents  (HBM GB/s)
+  decode_shared  16 contexts x 16384 keys, each read by all 4 agents (rank 16):
+              64 requests whose K/V tiles are streamed once per context (HBM GB/s,
+              shared rows counted once), also timed with grouping switched off
   precompute  L = X·[A_1..A_3], X [32768, 4096], ranks 3 x 64              (HBM GB/s)
   longctx     512 queries over 32768 keys, rank 64, L from the precompute   (TFLOP/s)
   mixed       (--mixed) 32 layers of a 32-request batch, ranks 8/16/32/64   (roofline time)
@@ -197,6 +200,34 @@ def bench_decode(steps, warmup, flush):
             "roofline": roof(gbs, accounting.PEAK_HBM_GBS, "GB/s", "hbm", traffic_bytes(prob.name))}
 
 
+def bench_decode_shared(steps, warmup, flush):
+    from shared_rank_kv_amd import accounting, lra, workloads
+    prob = workloads.decode_shared_batch()
+    t = time.time()
+    cpu, dev = upload(prob)
+    log(f"[bench] shared-context decode inputs ready in {time.time() - t:.1f}s")
+    ws = workspace_for(prob, True)
+    fn = lra.prepare_attn_decode(dev["Q"], dev["K"], dev["V"], dev["L"], dev["B"], prob.k_start,
+                                 prob.k_len, prob.agent_idx, O=torch_empty_like(dev["Q"]),
+                                 workspace=ws)
+    per, _ = time_calls(fn, steps, warmup, flush)
+    # the same calls with one work item per request (each request streams its context)
+    os.environ["LRA_DECODE_GROUP"] = "0"
+    try:
+        per1, _ = time_calls(fn, steps, warmup, flush)
+    finally:
+        del os.environ["LRA_DECODE_GROUP"]
+    flop, nbytes = accounting.attention_work(prob)
+    del dev, cpu
+    ms, ms1 = float(np.median(per)), float(np.median(per1))
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": prob.name, "value": round(gbs, 1), "unit": "GB/s",
+            "ms_per_call": round(ms, 4), "ms_min": round(float(per.min()), 4),
+            "ms_max": round(float(per.max()), 4), "bytes": nbytes, "flop": flop,
+            "ungrouped_ms_per_call": round(ms1, 4), "speedup_vs_ungrouped": round(ms1 / ms, 2),
+            "roofline": roof(gbs, accounting.PEAK_HBM_GBS, "GB/s", "hbm", traffic_bytes(prob.name))}
+
+
 def bench_longctx(steps, warmup, flush):
     import torch
     from shared_rank_kv_amd import accounting, lra, workloads
@@ -363,6 +394,8 @@ def run_only(args):
                 "read_bytes": 1 << 30, "write_bytes": 1 << 30}
     if args.only == "decode":
         return bench_decode(args.steps, args.warmup, Flusher())
+    if args.only == "decode_shared":
+        return bench_decode_shared(args.steps, args.warmup, Flusher())
     if args.only == "longctx":
         pre, lc = bench_longctx(args.steps, args.warmup, Flusher())
         return {"precompute": pre, "longctx_prefill": lc}
@@ -375,7 +408,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--mixed", action="store_true", help="also time the 32-layer mixed batch")
-    ap.add_argument("--only", choices=["prefill", "decode", "longctx", "mixed", "copy"],
+    ap.add_argument("--only", choices=["prefill", "decode", "decode_shared", "longctx", "mixed",
+                                       "copy"],
                     help="time one workload only (for profiling); prints its JSON object. "
                          "'copy' times a 1 GiB device copy, the reference for HBM counters")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -420,6 +454,8 @@ def main():
         flush = Flusher()
         log("[bench] decode")
         out["decode"] = bench_decode(args.steps, args.warmup, flush)
+        log("[bench] shared-context decode")
+        out["decode_shared"] = bench_decode_shared(args.steps, args.warmup, flush)
         log("[bench] precompute + long-context prefill")
         out["precompute"], out["longctx_prefill"] = bench_longctx(args.steps, args.warmup, flush)
         del flush

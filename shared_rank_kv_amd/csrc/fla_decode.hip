@@ -393,6 +393,365 @@ __global__ __launch_bounds__(256, 2) void fla_decode_bf16(const AttnArgs args) {
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// Shared-context decode.  Requests of different agents that read the same base rows (one
+// base cache shared by the agents: BaseShared in the LRAgent summary, section 2; with all
+// LR caches aliased, BaseLRShared) form a unit of up to kMaxMembers requests.  A work item
+// (unit, kv head, key split) streams each K/V_base tile once for every member: the
+// members' query heads fill the 16 columns of the score tile (column c is member c / G,
+// head c % G), so the one P·V_base product serves them all.  Only the LR term is per
+// member: every tile, each member's L rows pass through the wave's LR tile in turn and
+// (P·L_a)ᵀ += L_aᵀ·Pᵀ runs with P masked to that member's columns, so one accumulator
+// holds, in every column, the product with that column's own agent.  B_a is applied per
+// member when the wave states are merged.
+// (Ranks up to 32 keep two workgroups per CU, with a few registers spilled outside the key
+// loop; rank 64 needs the register file of one.)
+template <int D, int RB>
+__global__ __launch_bounds__(256, RB == 2 ? 1 : 2) void fla_decode_shared_bf16(const AttnArgs args) {
+  const AttnArgs* A = (const AttnArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+  constexpr int CPR = D / 8;                 // 16-byte chunks per K/V row
+  constexpr int DB = D / 16;                 // 16-row blocks of the transposed output
+  constexpr int KS = D / 32;                 // k-steps of the score product
+  constexpr int VT = kKeys * D * 2;          // V tile bytes (per wave)
+  constexpr int LT = kKeys * 64 * 2;         // LR tile bytes (per wave, rank <= 64)
+  constexpr int VLOADS = VT / 1024;          // 16-byte V loads per lane per tile
+  constexpr int NRB = RB > 0 ? RB * 2 : 1;   // 16-column blocks of the LR accumulator
+  constexpr int LCH = RB > 0 ? 4 * RB : 1;   // 16-byte chunks of the LR columns loaded per row
+  constexpr int NL = RB > 0 ? kKeys * LCH / 64 : 0;   // 16-byte L loads per lane per member
+  constexpr int NM = kMaxMembers;
+  constexpr int LOOP_LDS = 4 * (VT + LT);
+  constexpr int MERGE_LDS = (4 * 16 * D + 4 * 16 * 64 + 4 * 16 * 2 + 16 * 64) * 4;
+  __shared__ __attribute__((aligned(1024)))
+  char smem_raw[LOOP_LDS > MERGE_LDS ? LOOP_LDS : MERGE_LDS];
+  LDS char* smem = (LDS char*)smem_raw;
+
+  const int bid = blockIdx.x;
+  const int w = (bid & 7) * A->grid_per_xcd + (bid >> 3);
+  if (w >= A->n_work) return;
+  const int b = find_unit(A, w);
+  const ReqDesc& R = A->reqs[b];
+  const int nm = __builtin_amdgcn_readfirstlane(R.n_members);
+  const int k_start = R.k_start, Lk = R.k_len, n_split = R.n_split;
+  const int G = A->G, Hq = A->Hq, Hkv = A->Hkv;
+  const int local = w - R.work_start;
+  const int g = local % Hkv;
+  const int sp = local / Hkv;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar loop control
+  const int col = lane & 15, grp = lane >> 4;
+  const int mcol = col / G;                  // member of this lane's query column
+  const bool col_ok = mcol < nm;
+
+  // key range of this split, in 32-key tiles dealt round-robin to the 4 waves
+  const int n_tiles_req = (Lk + kKeys - 1) / kKeys;
+  const int tps = (n_tiles_req + n_split - 1) / n_split;
+  const int kb = sp * tps * kKeys;
+  const int ke = min(Lk, kb + tps * kKeys);
+  const int n_tiles = ke > kb ? (ke - kb + kKeys - 1) / kKeys : 0;
+  const int my_tiles = n_tiles > wave ? (n_tiles - wave + 3) / 4 : 0;
+
+  const int64_t kv_stride = (int64_t)Hkv * D;
+  const bf16* Kg = (const bf16*)A->K + ((int64_t)k_start * Hkv + g) * D;
+  const bf16* Vg = (const bf16*)A->V + ((int64_t)k_start * Hkv + g) * D;
+
+  // Q (B operand of Sᵀ = K·Qᵀ): lane holds Q[head g*G + col%G of member col/G]
+  bf16x8 qf[KS];
+  {
+    const int qs = col_ok ? A->reqs[b + mcol].q_start : 0;
+    const bf16* qrow = (const bf16*)A->Q + ((int64_t)qs * Hq + g * G + col % G) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qf[ks] = col_ok ? *(const bf16x8*)(qrow + ks * 32 + grp * 8) : bf16x8{};
+  }
+
+  LDS char* vt = smem + wave * (VT + LT);
+  LDS char* lt = vt + VT;
+
+  // LR rows of every member slot through a buffer resource that covers exactly the
+  // request's rows: reads past them, past the row's rank (the row continues into padding
+  // or the next row; those columns are never used), or of an empty slot return zeros
+  // or unused values and never leave the member's cache.  Each load unit u = lane + 64 i
+  // covers row u / LCH, 16-byte chunk u % LCH of the 32 x (32 RB) tile.
+  __amdgpu_buffer_rsrc_t lrs[NM];
+  int ldl_b[NM];
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+    int bytes = 0;
+    const void* base = A->K;
+    ldl_b[m] = 0;
+    if (RB && m < nm) {
+      const AgentDesc& AG = A->agents[A->reqs[b + m].agent];
+      if (AG.rank > 0) {
+        base = (const bf16*)AG.L + (int64_t)k_start * AG.ldl;
+        bytes = (int)((int64_t)Lk * AG.ldl * 2);
+        ldl_b[m] = (int)(AG.ldl * 2);
+      }
+    }
+    ldl_b[m] = __builtin_amdgcn_readfirstlane(ldl_b[m]);
+    lrs[m] = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0,
+                                               __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+  }
+  int l_row[NL > 0 ? NL : 1], l_dst[NL > 0 ? NL : 1];
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const int u = lane + 64 * i;
+    l_row[i] = u / LCH;
+    l_dst[i] = (u / LCH) * 128 + (u % LCH) * 16;
+  }
+
+  u32x4 kreg[2][KS];
+  u32x4 vreg[VLOADS];
+  u32x4 lreg[NM][NL > 0 ? NL : 1];
+  // Tiles past the wave's last one clamp to key ke-1: the loop prefetches without branches.
+  auto tile_key = [&](int jt) { return kb + (wave + 4 * jt) * kKeys; };
+  auto load_k = [&](int jt) {
+    const int k0 = tile_key(jt);
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      const int key = min(k0 + kb2 * 16 + col, ke - 1);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        kreg[kb2][ks] = *(const u32x4*)(Kg + (int64_t)key * kv_stride + (ks * 4 + grp) * 8);
+    }
+  };
+  auto load_v = [&](int jt) {
+    const int k0 = tile_key(jt);
+#pragma unroll
+    for (int i = 0; i < VLOADS; ++i) {
+      const int key = min(k0 + i * (64 / CPR) + lane / CPR, ke - 1);
+      vreg[i] = *(const u32x4*)(Vg + (int64_t)key * kv_stride + (lane % CPR) * 8);
+    }
+  };
+  // every member slot loads, unconditionally (empty slots read zeros without memory traffic)
+  auto load_l = [&](int jt) {
+    const int k0 = tile_key(jt);
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        const int key = min(k0 + l_row[i], ke - 1);
+        const int u = lane + 64 * i;
+        lreg[m][i] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(lrs[m], key * ldl_b[m] + (u % LCH) * 16,
+                                                         0, 0));
+      }
+  };
+  auto store_v = [&]() {
+#pragma unroll
+    for (int i = 0; i < VLOADS; ++i) {
+      const int row = i * (64 / CPR) + lane / CPR;
+      const int c = (lane % CPR) ^ vswz<D>(row);
+      *(LDS u32x4*)(vt + row * (D * 2) + c * 16) = vreg[i];
+    }
+  };
+
+  // transposing-read offsets: lane (e = (lane&15)/4, q = lane&3) of group grp supplies
+  // 4 bf16 of key row grp*4 + e (and 16 + grp*4 + e), columns 16-block + 4q
+  int voff[DB];
+  const int trow = grp * 4 + ((lane & 15) >> 2), tq = lane & 3;
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    const int d = db * 16 + tq * 4;
+    voff[db] = trow * (D * 2) + (((d >> 3) ^ vswz<D>(trow)) << 4) + (d & 7) * 2;
+  }
+
+  f32x4 acc[DB];
+  f32x4 accl[NRB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) acc[i] = f32x4{};
+#pragma unroll
+  for (int i = 0; i < NRB; ++i) accl[i] = f32x4{};
+  float m_run = kNegBig, l_run = 0.f;
+  const float sl2 = A->scale_log2;
+
+  // K is loaded one tile ahead into registers, V two tiles ahead (registers, then the
+  // wave's V tile), each member's L rows one tile ahead into registers.
+  if (my_tiles > 0) {
+    load_k(0);
+    load_v(0);
+    if (RB) load_l(0);
+    store_v();
+    load_v(1);
+    for (int jt = 0; jt < my_tiles; ++jt) {
+      const int k0 = tile_key(jt);
+      f32x4 s[2];
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+        s[kb2] = f32x4{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          s[kb2] = mfma16(__builtin_bit_cast(bf16x8, kreg[kb2][ks]), qf[ks], s[kb2]);
+      }
+      load_k(jt + 1);
+      const int lim = ke - 1 - k0 - grp * 4;
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (kb2 * 16 + j > lim) s[kb2][j] = -INFINITY;
+      float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                       fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+      mx = col_max(mx) * sl2;
+      if (__any(mx > m_run + kRescaleSlack)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int i = 0; i < DB; ++i) acc[i] *= alpha;
+#pragma unroll
+        for (int i = 0; i < NRB; ++i) accl[i] *= alpha;
+      }
+      bf16x8 pf;
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[kb2][j], sl2, -m_run));
+          l_run += p;
+          pf[kb2 * 4 + j] = (bf16)p;
+        }
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        acc[db] = mfma16(join(tr_read(vt + voff[db]), tr_read(vt + voff[db] + 16 * D * 2)), pf,
+                         acc[db]);
+      if (RB) {
+        // one member at a time through the LR tile: this wave's reads of member m precede
+        // the writes of member m + 1 in program order, and the LDS executes one wave's
+        // operations in order
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+          if (m >= nm) break;
+#pragma unroll
+          for (int i = 0; i < NL; ++i) *(LDS u32x4*)(lt + l_dst[i]) = lreg[m][i];
+          const bf16x8 pm = mcol == m ? pf : bf16x8{};
+#pragma unroll
+          for (int rb = 0; rb < NRB; ++rb) {
+            const LDS char* p = lt + trow * 128 + (rb * 16 + tq * 4) * 2;
+            accl[rb] = mfma16(join(tr_read(p), tr_read(p + 16 * 128)), pm, accl[rb]);
+          }
+        }
+      }
+      if (RB) load_l(jt + 1);
+      // the next tile's V replaces this one: this wave's reads above precede the writes
+      store_v();
+      load_v(jt + 2);
+    }
+  }
+
+  // ---- merge the 4 wave states through LDS, apply each member's B_a, store
+  // Output mapping: thread (slot, dp) produces the d pair 2 dp of every query column of
+  // member `slot` (its G heads), so it needs that member's B_a column pair only: the rank
+  // rows go to registers now, before the merge, whose barriers hide their latency.
+  constexpr int TPC = D / 2;                 // threads per d range
+  constexpr int RMAX = RB > 0 ? 32 * RB : 1;
+  const int dp = tid % TPC, slot = tid / TPC;
+  bf16x2 bpre[RMAX];
+  int brank = 0;
+  if (RB && slot < nm) {
+    const AgentDesc& AG = A->agents[A->reqs[b + slot].agent];
+    brank = AG.rank;
+    // rows past the rank read zeros (bounds of the resource), so the loads are unconditional
+    const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((const bf16*)AG.B + g * D), (short)0,
+        (int)((int64_t)brank * kv_stride * 2), 0x00020000);
+#pragma unroll
+    for (int k = 0; k < RMAX; ++k)
+      bpre[k] = __builtin_bit_cast(
+          bf16x2, __builtin_amdgcn_raw_buffer_load_b32(br, (int)((k * kv_stride + 2 * dp) * 2),
+                                                       0, 0));
+  }
+  const float l_col = col_sum(l_run);
+  __syncthreads();   // every wave is done with its tiles
+  LDS float* sh = (LDS float*)smem;              // [wave][16 cols][D]   P·V_base
+  LDS float* shl = sh + 4 * 16 * D;              // [wave][16 cols][64]  P·L_a
+  LDS float* shm = shl + 4 * 16 * 64;            // [wave][16 cols][2]   (m, l)
+  LDS float* sa = shm + 4 * 16 * 2;              // [16 cols][64]        merged P·L_a
+  if (col_ok) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sh[(wave * 16 + col) * D + db * 16 + grp * 4 + j] = acc[db][j];
+    if (RB) {
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          shl[(wave * 16 + col) * 64 + rb * 16 + grp * 4 + j] = accl[rb][j];
+    }
+    if (grp == 0) {
+      shm[(wave * 16 + col) * 2] = m_run;
+      shm[(wave * 16 + col) * 2 + 1] = l_col;
+    }
+  }
+  __syncthreads();
+
+  auto weights = [&](int c, float* wgt, float& M, float& l) {
+    M = kNegBig;
+#pragma unroll
+    for (int wv = 0; wv < 4; ++wv) M = fmaxf(M, shm[(wv * 16 + c) * 2]);
+    l = 0.f;
+#pragma unroll
+    for (int wv = 0; wv < 4; ++wv) {
+      wgt[wv] = __builtin_amdgcn_exp2f(shm[(wv * 16 + c) * 2] - M);
+      l += wgt[wv] * shm[(wv * 16 + c) * 2 + 1];
+    }
+  };
+  const int ncols = nm * G;
+  if (RB) {
+    // merged P·L_a of every (column, rank index) the outputs use
+    for (int e = tid; e < 16 * RMAX; e += 256) {
+      const int c = e / RMAX, rho = e % RMAX;
+      if (c < ncols) {
+        float wgt[4], M, l;
+        weights(c, wgt, M, l);
+        float v = 0.f;
+#pragma unroll
+        for (int wv = 0; wv < 4; ++wv) v += wgt[wv] * shl[(wv * 16 + c) * 64 + rho];
+        sa[c * 64 + rho] = v;
+      }
+    }
+    __syncthreads();
+  }
+  if (slot < nm) {
+    const ReqDesc& Rm = A->reqs[b + slot];
+    for (int hh = 0; hh < G; ++hh) {
+      const int c = slot * G + hh;
+      float wgt[4], M, l;
+      weights(c, wgt, M, l);
+      float o0 = 0.f, o1 = 0.f;
+#pragma unroll
+      for (int wv = 0; wv < 4; ++wv) {
+        const f32x2 v = *(const LDS f32x2*)(sh + (wv * 16 + c) * D + 2 * dp);
+        o0 += wgt[wv] * v[0];
+        o1 += wgt[wv] * v[1];
+      }
+      if (RB) {
+        // columns of P·L_a past the member's rank hold unrelated products: skipped
+#pragma unroll
+        for (int k = 0; k < RMAX; ++k) {
+          if (k < brank) {
+            const float a = sa[c * 64 + k];
+            o0 += a * (float)bpre[k][0];
+            o1 += a * (float)bpre[k][1];
+          }
+        }
+      }
+      const int h = g * G + hh;
+      if (n_split == 1) {
+        const float inv = 1.f / l;
+        bf16x2 ob = {(bf16)(o0 * inv), (bf16)(o1 * inv)};
+        *(bf16x2*)((bf16*)A->O + ((int64_t)Rm.q_start * Hq + h) * D + 2 * dp) = ob;
+      } else {
+        const int64_t pr = (int64_t)Rm.part_base + (int64_t)sp * Hq + h;
+        *(float2*)(A->ws_o + pr * D + 2 * dp) = float2{o0, o1};
+        if (dp == 0) *(float2*)(A->ws_ml + pr * 2) = float2{M, l};
+      }
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_decode_bf16(const AttnArgs& a, int head_dim, int max_rank, int n_grid,
@@ -400,6 +759,24 @@ hipError_t launch_decode_bf16(const AttnArgs& a, int head_dim, int max_rank, int
   const int rb = max_rank > 32 ? 2 : (max_rank > 0 ? 1 : 0);
 #define LRA_LAUNCH(D, RB) \
   hipLaunchKernelGGL((fla_decode_bf16<D, RB>), dim3(n_grid), dim3(kThreads), 0, s, a)
+  if (head_dim == 128) {
+    if (rb == 0) LRA_LAUNCH(128, 0);
+    else if (rb == 1) LRA_LAUNCH(128, 1);
+    else LRA_LAUNCH(128, 2);
+  } else {
+    if (rb == 0) LRA_LAUNCH(64, 0);
+    else if (rb == 1) LRA_LAUNCH(64, 1);
+    else LRA_LAUNCH(64, 2);
+  }
+#undef LRA_LAUNCH
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_shared_bf16(const AttnArgs& a, int head_dim, int max_rank, int n_grid,
+                                     hipStream_t s) {
+  const int rb = max_rank > 32 ? 2 : (max_rank > 0 ? 1 : 0);
+#define LRA_LAUNCH(D, RB) \
+  hipLaunchKernelGGL((fla_decode_shared_bf16<D, RB>), dim3(n_grid), dim3(kThreads), 0, s, a)
   if (head_dim == 128) {
     if (rb == 0) LRA_LAUNCH(128, 0);
     else if (rb == 1) LRA_LAUNCH(128, 1);

@@ -9,6 +9,8 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <map>
+#include <utility>
 #include <vector>
 
 #include "lra_internal.h"
@@ -33,6 +35,12 @@ int ok() {
 bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Shared-context decode grouping is on unless LRA_DECODE_GROUP=0 (kept for comparisons).
+bool group_decode_enabled() {
+  const char* v = std::getenv("LRA_DECODE_GROUP");
+  return !(v && v[0] == '0' && v[1] == '\0');
+}
 
 int env_int(const char* name, int dflt) {
   const char* v = std::getenv(name);
@@ -253,10 +261,92 @@ int run_attention(const AttnShape& s, bool decode, const Requests& rq, const voi
     a.agents[i].rank = ad.ranks[i];
   }
   const size_t n = p.active.size();
-  for (size_t c0 = 0; c0 < n; c0 += lra::kReqsPerLaunch) {
-    const size_t c1 = std::min(n, c0 + lra::kReqsPerLaunch);
+  // Units: requests that one work item serves together.  Decode requests that read the same
+  // base rows (equal k_start and k_len) share every K/V tile, so they are grouped, up to
+  // kMaxMembers (and 16 / G query columns) per unit, members consecutive in launch order;
+  // every other request is a unit of its own.
+  std::vector<int> unit_size(n, 1);
+  if (decode && s.dtype == LRA_DTYPE_BF16 && group_decode_enabled()) {
+    const int cap = std::min(lra::kMaxMembers, 16 / G);
+    bool fits = cap >= 2;
+    for (size_t i = 0; i < n && fits; ++i) {
+      const int b = p.active[i];
+      const int a = rq.agent[b];
+      if (ad.ranks[a] > 0 && (int64_t)rq.k_len[b] * ad.ldl[a] * 2 >= ((int64_t)1 << 31))
+        fits = false;   // the kernel addresses one request's LR rows with 32-bit offsets
+    }
+    if (fits) {
+      std::map<std::pair<int32_t, int32_t>, std::vector<size_t>> groups;
+      std::vector<std::pair<int32_t, int32_t>> first_seen;
+      for (size_t i = 0; i < n; ++i) {
+        const int b = p.active[i];
+        const auto key = std::make_pair(rq.k_start[b], rq.k_len[b]);
+        auto it = groups.find(key);
+        if (it == groups.end()) {
+          first_seen.push_back(key);
+          groups[key].push_back(i);
+        } else {
+          it->second.push_back(i);
+        }
+      }
+      std::vector<size_t> order;
+      unit_size.clear();
+      for (const auto& key : first_seen) {
+        const auto& mem = groups[key];
+        for (size_t j = 0; j < mem.size(); j += cap) {
+          const size_t cnt = std::min(mem.size() - j, (size_t)cap);
+          unit_size.push_back((int)cnt);
+          for (size_t k = 0; k < cnt; ++k) order.push_back(mem[j + k]);
+        }
+      }
+      Plan q = p;
+      for (size_t i = 0; i < n; ++i) {
+        p.active[i] = q.active[order[i]];
+        p.n_rt[i] = q.n_rt[order[i]];
+        p.n_split[i] = q.n_split[order[i]];
+        p.part_base[i] = q.part_base[order[i]];
+      }
+      // A unit's work item streams its K/V once for every member, so it takes about
+      // `members` times the keys of a single request's split: the fixed cost of a work
+      // item (first loads in flight, the merge) is spread over more work.  At least two
+      // work items per CU remain, and a unit never has more splits than its members would
+      // alone, so the workspace size (which the query computes without grouping) and the
+      // members' partial-row ranges still hold.
+      const int chunk = env_int("LRA_DECODE_CHUNK", 1024);
+      std::vector<int> split_u(unit_size.size());
+      int64_t items = 0;
+      for (size_t u = 0, i = 0; u < unit_size.size(); i += unit_size[u++]) {
+        const int64_t kl = rq.k_len[p.active[i]];
+        split_u[u] = unit_size[u] < 2 ? p.n_split[i]
+                     : (int)std::max<int64_t>(1, std::min<int64_t>(
+                           p.n_split[i], ceil_div(kl, (int64_t)chunk * unit_size[u])));
+        items += (int64_t)s.Hkv * split_u[u];
+      }
+      const int64_t min_items = 2 * 256;
+      if (items < min_items) {
+        const int64_t f = ceil_div(min_items, std::max<int64_t>(items, 1));
+        for (size_t u = 0, i = 0; u < unit_size.size(); i += unit_size[u++])
+          if (unit_size[u] > 1)
+            split_u[u] = (int)std::min<int64_t>(p.n_split[i], (int64_t)split_u[u] * f);
+      }
+      for (size_t u = 0, i = 0; u < unit_size.size(); i += unit_size[u++])
+        for (int k = 0; k < unit_size[u]; ++k) p.n_split[i + k] = split_u[u];
+    }
+  }
+  const int heads_per_item = s.dtype == LRA_DTYPE_F32 ? s.Hq : s.Hkv;
+  size_t c0 = 0, u0 = 0;
+  while (c0 < n) {
+    // whole units, at most kReqsPerLaunch requests per launch
+    size_t c1 = c0, u1 = u0;
+    bool shared = false;
+    while (u1 < unit_size.size() && c1 - c0 + unit_size[u1] <= (size_t)lra::kReqsPerLaunch) {
+      shared |= unit_size[u1] > 1;
+      c1 += unit_size[u1++];
+    }
     int64_t work = 0, comb = 0;
     a.n_req = (int)(c1 - c0);
+    size_t next_leader = c0;
+    size_t u = u0;
     for (size_t i = c0; i < c1; ++i) {
       const int b = p.active[i];
       lra::ReqDesc& r = a.reqs[i - c0];
@@ -267,11 +357,17 @@ int run_attention(const AttnShape& s, bool decode, const Requests& rq, const voi
       r.agent = rq.agent[b];
       r.n_rt = p.n_rt[i];
       r.n_split = p.n_split[i];
-      r.work_start = (int)work;
       r.part_base = (int)p.part_base[i];
       r.comb_start = (int)comb;
-      const int heads_per_item = s.dtype == LRA_DTYPE_F32 ? s.Hq : s.Hkv;
-      work += (int64_t)heads_per_item * r.n_rt * r.n_split;
+      if (i == next_leader) {   // first member of unit u: owns the unit's work items
+        r.work_start = (int)work;
+        r.n_members = unit_size[u];
+        work += (int64_t)heads_per_item * r.n_rt * r.n_split;
+        next_leader += unit_size[u++];
+      } else {
+        r.work_start = INT32_MAX;
+        r.n_members = 0;
+      }
       if (r.n_split > 1) comb += (int64_t)r.q_len * s.Hq;
     }
     if (work > INT32_MAX / 2) return fail(LRA_ERR_UNSUPPORTED, "launch too large");
@@ -283,14 +379,20 @@ int run_attention(const AttnShape& s, bool decode, const Requests& rq, const voi
       a.grid_per_xcd = grid / 8;
       int max_rank = 0;
       for (size_t i = c0; i < c1; ++i) max_rank = std::max(max_rank, ad.ranks[rq.agent[p.active[i]]]);
-      e = decode ? lra::launch_decode_bf16(a, s.D, max_rank, grid, stream)
-                 : lra::launch_prefill_bf16(a, s.D, max_rank, grid, stream);
+      if (!decode)
+        e = lra::launch_prefill_bf16(a, s.D, max_rank, grid, stream);
+      else if (shared)
+        e = lra::launch_decode_shared_bf16(a, s.D, max_rank, grid, stream);
+      else
+        e = lra::launch_decode_bf16(a, s.D, max_rank, grid, stream);
       if (e == hipSuccess && comb > 0) e = lra::launch_combine_bf16(a, s.D, stream);
     } else {
       a.grid_per_xcd = 0;
       e = lra::launch_attn_f32(a, s.D, (int)work, stream);
     }
     if (e != hipSuccess) return fail(LRA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    c0 = c1;
+    u0 = u1;
   }
   return ok();
 }

@@ -14,6 +14,16 @@ __device__ __forceinline__ int find_request(const AttnArgs* A, int w) {
   return __builtin_amdgcn_readfirstlane(__popcll(__ballot(start <= w)) - 1);
 }
 
+// Unit of the shared-context decode kernel that owns work item w (wave-uniform): the last
+// request whose work start is <= w.  Unit members other than the first hold INT32_MAX and
+// never match; the starts of the first members increase strictly.
+__device__ __forceinline__ int find_unit(const AttnArgs* A, int w) {
+  const int lane = threadIdx.x & 63;
+  const int start = lane < A->n_req ? A->reqs[lane].work_start : 0x7fffffff;
+  const unsigned long long m = __ballot(start <= w);
+  return __builtin_amdgcn_readfirstlane(63 - __clzll(m));
+}
+
 // Request that owns combine row `row` (per thread): combine starts are a non-decreasing
 // prefix sum over requests (zero rows for requests without key splits), so the owner is
 // the last request whose start is <= row.  Binary search over the starts held one per

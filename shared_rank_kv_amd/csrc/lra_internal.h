@@ -39,7 +39,15 @@ struct ReqDesc {
   int32_t work_start;  // first work item of this request within the launch
   int32_t part_base;   // first partial row in the workspace (split requests), else -1
   int32_t comb_start;  // first combine row of this request within the launch
+  // Shared-context decode: requests that read the same base rows are grouped into units
+  // of consecutive entries.  The first entry of a unit owns its work items and holds the
+  // member count; the other members hold 0 here and work_start = INT32_MAX.
+  int32_t n_members;
 };
+
+// Members per unit of the shared-context decode kernel (at most 16 / G: the members'
+// query heads share the 16 columns of one MFMA tile).
+constexpr int kMaxMembers = 4;
 
 struct AttnArgs {
   const void* Q;
@@ -75,6 +83,8 @@ struct PrecomputeArgs {
 // Launchers (return the HIP status of the launch).
 hipError_t launch_prefill_bf16(const AttnArgs& a, int head_dim, int max_rank, int n_grid,
                                hipStream_t s);
+hipError_t launch_decode_shared_bf16(const AttnArgs& a, int head_dim, int max_rank, int n_grid,
+                                     hipStream_t s);
 hipError_t launch_decode_bf16(const AttnArgs& a, int head_dim, int max_rank, int n_grid,
                               hipStream_t s);
 hipError_t launch_combine_bf16(const AttnArgs& a, int head_dim, hipStream_t s);

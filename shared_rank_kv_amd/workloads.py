@@ -176,6 +176,14 @@ def decode_batch():
         kv_rows=batch * ctx, seed=seed, std_b=0.05)
 
 
+def decode_shared_batch():
+    """Shared-context decode, bf16: 16 contexts of 16384 tokens, each read by all 4 agents
+    (rank 16) with one query token apiece: 64 requests, 32 q / 8 kv heads, head_dim 128.
+    Every agent keeps its own LR cache over all contexts (the PreLRShared layout)."""
+    return shared_decode("decode-shared-16x4x16384-r16", 32, 8, 128, (16, 16, 16, 16),
+                         [(16384, [0, 1, 2, 3])] * 16, seed=SEED_BASE + 5)
+
+
 def longctx_precompute():
     """LR precompute for the 32768-token context: X [32768, 4096] ~ N(0,1), three agents'
     A_a [4096, 64] ~ N(0, 1/4096)."""
@@ -221,6 +229,25 @@ def mixed_batch_layer(layer):
 
 
 MIXED_LAYERS = 32
+
+
+def shared_decode(name, n_q_heads, n_kv_heads, head_dim, ranks, contexts, seed, order=None,
+                  std_b=0.05):
+    """bf16 decode over shared contexts: contexts = [(k_len, [agent, ...]), ...]; each listed
+    agent has one request (one query token) over that context's base rows, and reads its own
+    LR cache over the same rows.  `order` permutes the requests (default: context by
+    context)."""
+    starts = np.concatenate([[0], np.cumsum([kl for kl, _ in contexts])[:-1]]).astype(np.int64)
+    reqs = [(int(starts[c]), int(kl), int(a)) for c, (kl, ags) in enumerate(contexts) for a in ags]
+    if order is not None:
+        reqs = [reqs[i] for i in order]
+    n = len(reqs)
+    return AttnProblem(
+        name=name, dtype="bf16", n_q_heads=n_q_heads, n_kv_heads=n_kv_heads, head_dim=head_dim,
+        ranks=tuple(ranks), q_start=np.arange(n, dtype=np.int32), q_len=np.ones(n, np.int32),
+        k_start=_i32([r[0] for r in reqs]), k_len=_i32([r[1] for r in reqs]),
+        agent_idx=_i32([r[2] for r in reqs]), q_rows=n,
+        kv_rows=int(sum(kl for kl, _ in contexts)), seed=seed, std_b=std_b)
 
 
 def custom(name, dtype, n_q_heads, n_kv_heads, head_dim, ranks, q_len, k_len, agent_idx,

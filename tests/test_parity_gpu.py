@@ -175,6 +175,49 @@ def test_bf16_decode_shapes(shape, chunk, monkeypatch):
     _cmp_full(prob, cpu, H.run_decode(prob, dev))
 
 
+# Shared contexts in decode (BaseShared): requests that read the same base rows are served
+# by one work item.  (D, Hq, Hkv, ranks, contexts): units of 4 members (G = 4), of 2 (G = 8),
+# of 4 with one column per member (G = 1); member counts that are not a multiple of the unit
+# size; the same agent twice in a unit; rank-0, rank-8 and rank-64 agents in one unit; key
+# counts around the 32-key tile.
+SHARED_DECODE = [
+    (128, 32, 8, (16, 16, 16, 16), [(2000, [0, 1, 2, 3]), (700, [3, 2, 1]), (33, [0, 0]),
+                                    (5000, [1])]),
+    (64, 16, 2, (64, 0, 8), [(1500, [0, 1, 2, 0, 1, 2, 0])]),
+    (128, 8, 8, (32, 24), [(900, [0, 1, 0, 1, 0, 1]), (64, [1, 0])]),
+    (128, 16, 8, (64, 64, 64), [(4100, [0, 1, 2]), (1, [2, 1])]),
+]
+
+
+@pytest.mark.parametrize("shape", SHARED_DECODE, ids=lambda s: f"D{s[0]}-Hq{s[1]}-Hkv{s[2]}-r{max(s[3])}")
+@pytest.mark.parametrize("chunk", ["64", "1024"])
+def test_bf16_decode_shared_contexts(shape, chunk, monkeypatch):
+    monkeypatch.setenv("LRA_DECODE_CHUNK", chunk)
+    D, Hq, Hkv, ranks, contexts = shape
+    n = sum(len(a) for _, a in contexts)
+    order = np.random.default_rng(n + D).permutation(n)     # members interleaved in the batch
+    prob = workloads.shared_decode("bf16-decode-shared", Hq, Hkv, D, ranks, contexts,
+                                   seed=680 + D + Hq, order=order)
+    cpu, dev = H.device_inputs(prob)
+    grouped = H.run_decode(prob, dev)
+    _cmp_full(prob, cpu, grouped)
+    again = H.run_decode(prob, dev)
+    assert torch.equal(grouped, again), "repeat call not bitwise identical"
+    monkeypatch.setenv("LRA_DECODE_GROUP", "0")
+    single = H.run_decode(prob, dev)
+    assert (grouped.float() - single.float()).abs().max().item() <= 4e-3
+
+
+def test_bf16_decode_shared_lr_cache():
+    # BaseLRShared: every agent's LR cache is one buffer; the B_a still differ
+    prob = workloads.shared_decode("bf16-decode-lrshared", 32, 8, 128, (16, 16, 16),
+                                   [(3000, [0, 1, 2]), (800, [2, 0])], seed=690)
+    cpu, dev = H.device_inputs(prob)
+    cpu["L"] = [cpu["L"][0]] * 3
+    dev["L"] = [dev["L"][0]] * 3
+    _cmp_full(prob, cpu, H.run_decode(prob, dev), what="shared LR cache")
+
+
 # ---------------------------------------------------------------------------------------
 # LR precompute
 # ---------------------------------------------------------------------------------------
