@@ -102,12 +102,13 @@ def time_calls(fn, steps, warmup, flush=None):
 # what the same counter reads for a plain 1 GiB device copy); the per-kernel summaries and
 # the commands are under profiles/.  The figures describe the kernels built from sources
 # with this digest and are reported as null for any other sources.
-TRAFFIC_SOURCES_SHA256 = "557589b0c892eb3ad6383ee95dcb6464ecd8f300ef6644c4b47720efc2b02ec6"
+TRAFFIC_SOURCES_SHA256 = "6013db3b93d9433766d8dbef48897916a7f5158a2fba17152d5f8108d5c175a8"
 TRAFFIC_BYTES = {
-    "llama8b-prefill-1024q-9216k-r16": 127035520,
-    "decode-64x16384-r16": 4418271946,
-    "lr-precompute-32768x4096-3x64": 293965514,
-    "longctx-prefill-512q-32768k-r64": 245419210,
+    "llama8b-prefill-1024q-9216k-r16": 127036105,
+    "decode-64x16384-r16": 4419107254,
+    "decode-shared-16x4x16384-r16": 1161952109,
+    "lr-precompute-32768x4096-3x64": 293966016,
+    "longctx-prefill-512q-32768k-r64": 245418831,
 }
 
 

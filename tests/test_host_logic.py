@@ -100,6 +100,21 @@ def test_attention_work_decode_and_long_context():
     assert round(nbytes / 1e6, 1) == 146.9
 
 
+def test_decode_shared_batch_work():
+    p = workloads.decode_shared_batch()
+    assert p.batch == 64 and p.kv_rows == 16 * 16384
+    # four requests per context, one per agent, all reading the context's rows
+    for c in range(16):
+        assert (p.k_start[4 * c:4 * c + 4] == c * 16384).all()
+        assert sorted(p.agent_idx[4 * c:4 * c + 4].tolist()) == [0, 1, 2, 3]
+    _, nbytes = accounting.attention_work(p)
+    kv = 16 * 16384 * 8 * 128 * 2 * 2          # each context's K/V rows once
+    lr = 64 * 16384 * 16 * 2                   # every request's own LR rows
+    b = 4 * 16 * 1024 * 2
+    qo = 64 * 32 * 128 * 2 * 2
+    assert nbytes == kv + lr + b + qo == 1108475904
+
+
 def test_shared_rows_count_once():
     # two requests reading the same base rows: K/V bytes counted once, LR rows per request
     p = workloads.custom("s", "bf16", 8, 2, 64, (16,), [4, 4], [100, 100], [0, 0], seed=1,

@@ -1,4 +1,4 @@
-"""GPU parity at the five workloads' full sizes, in the launch configuration the benchmark
+"""GPU parity at the benchmark workloads' full sizes, in the launch configuration the benchmark
 times, on outputs sampled so the fp64 oracle can evaluate them row by row."""
 
 import numpy as np
@@ -41,6 +41,15 @@ def test_decode_64x16k():
     O = H.run_decode(prob, dev)
     reqs = sorted(RNG.choice(prob.batch, size=8, replace=False).tolist() + [0, prob.batch - 1])
     _check_sampled(prob, cpu, O, sorted(set(reqs)), 1, "decode 64x16384")
+
+
+def test_decode_shared_16x4x16k():
+    # every member of the first and last context, and a random request of every other one
+    prob = workloads.decode_shared_batch()
+    cpu, dev = H.device_inputs(prob)
+    O = H.run_decode(prob, dev)
+    reqs = [0, 1, 2, 3, 60, 61, 62, 63] + [4 * c + int(RNG.integers(4)) for c in range(1, 15)]
+    _check_sampled(prob, cpu, O, sorted(set(reqs)), 1, "shared-context decode 16x4x16384")
 
 
 def test_longctx_precompute_then_prefill():
