@@ -226,6 +226,9 @@ def bench_decode_shared(steps, warmup, flush):
             "ms_per_call": round(ms, 4), "ms_min": round(float(per.min()), 4),
             "ms_max": round(float(per.max()), 4), "bytes": nbytes, "flop": flop,
             "ungrouped_ms_per_call": round(ms1, 4), "speedup_vs_ungrouped": round(ms1 / ms, 2),
+            # analytic KV-cache bytes of the batch's 16 contexts over 32 layers, per scheme
+            "cache_GB_32_layers": {k: round(16 * v / 1e9, 3) for k, v in accounting.cache_memory(
+                16384, prob.ranks, prob.n_kv_heads, prob.head_dim, 32).items()},
             "roofline": roof(gbs, accounting.PEAK_HBM_GBS, "GB/s", "hbm", traffic_bytes(prob.name))}
 
 

@@ -79,3 +79,46 @@ def precompute_work(p):
     R = sum(p.ranks)
     flop = 2 * p.T * p.d_model * R
     return flop, (p.T * p.d_model + p.d_model * R + p.T * R) * e
+
+
+# ---------------------------------------------------------------------------------------
+# KV-cache memory of the sharing schemes (LRAgent summary, section 2; PReCache abstract)
+# ---------------------------------------------------------------------------------------
+
+SCHEMES = ("non_shared", "base_shared", "base_lr_shared", "pre_lr_shared", "full_shared")
+
+
+def cache_memory(tokens, ranks, n_kv_heads, head_dim, n_layers=32, dtype="bf16",
+                 shared_rank=None):
+    """Bytes of KV cache that `len(ranks)` agents keep for one shared context of `tokens`
+    tokens, per sharing scheme (all layers):
+
+    * non_shared: every agent its own K and V caches (the adapter output folded in);
+    * base_shared: one base K/V cache for all agents, plus each agent's LR cache
+      [tokens, r_a] (the adapter's down-projection activations, x·A_a);
+    * base_lr_shared: one base K/V cache and one LR cache [tokens, shared_rank] for all
+      agents (a shared down-projection A makes the LR caches equal); shared_rank defaults
+      to the largest rank;
+    * pre_lr_shared: the memory of base_shared; every agent's LR cache is computed in one
+      pass over the shared context instead of on each switch of agent;
+    * full_shared: one K/V cache for all agents, no adapter state (the bound of sharing).
+    Keys are not decomposed: only the value side carries the adapter term."""
+    e = _elem(dtype)
+    n = len(ranks)
+    kv = 2 * n_kv_heads * head_dim * tokens * n_layers * e          # one K + V cache
+    lr_each = sum(ranks) * tokens * n_layers * e
+    r_shared = max(ranks) if shared_rank is None else shared_rank
+    lr_one = r_shared * tokens * n_layers * e
+    return {"non_shared": n * kv, "base_shared": kv + lr_each, "base_lr_shared": kv + lr_one,
+            "pre_lr_shared": kv + lr_each, "full_shared": kv}
+
+
+def cache_memory_summary(tokens, ranks, n_kv_heads, head_dim, n_layers=32, dtype="bf16"):
+    """cache_memory plus the two ratios the pages state in words: BaseShared against
+    Non-Shared (about 1/N) and the LR caches' share of BaseShared (small)."""
+    m = cache_memory(tokens, ranks, n_kv_heads, head_dim, n_layers, dtype)
+    n = len(ranks)
+    return {"bytes": m, "agents": n,
+            "base_over_non_shared": m["base_shared"] / m["non_shared"],
+            "one_over_n": 1.0 / n,
+            "lr_share_of_base_shared": (m["base_shared"] - m["full_shared"]) / m["base_shared"]}

@@ -115,6 +115,43 @@ def test_decode_shared_batch_work():
     assert nbytes == kv + lr + b + qo == 1108475904
 
 
+def test_cache_memory_closed_forms():
+    # Llama-3-8B shapes (8 kv heads x 128, 32 layers, bf16), 4 agents of rank 16, 16384 tokens
+    m = accounting.cache_memory(16384, (16, 16, 16, 16), 8, 128)
+    full = 2 * 8 * 128 * 16384 * 32 * 2
+    assert m["full_shared"] == full == 2 ** 31
+    assert m["non_shared"] == 4 * full
+    assert m["base_shared"] == m["pre_lr_shared"] == full + 4 * 16 * 16384 * 32 * 2
+    assert m["base_lr_shared"] == full + 16 * 16384 * 32 * 2
+    s = accounting.cache_memory_summary(16384, (16, 16, 16, 16), 8, 128)
+    assert s["base_over_non_shared"] == (2048 + 64) / (4 * 2048)
+    assert abs(s["lr_share_of_base_shared"] - 1 / 33) < 1e-15      # 64 / (2048 + 64)
+
+
+def test_cache_memory_invariants():
+    for ranks in ((8,), (16, 16, 16), (8, 16, 32, 64), (0, 0, 0, 0)):
+        m = accounting.cache_memory(1000, ranks, 4, 64, n_layers=3)
+        n = len(ranks)
+        assert m["non_shared"] == n * m["full_shared"]
+        assert m["full_shared"] <= m["base_lr_shared"] <= m["base_shared"]
+        if n == 1:
+            assert m["base_lr_shared"] == m["base_shared"]
+    # without adapter state BaseShared is exactly 1/N of Non-Shared
+    s = accounting.cache_memory_summary(1000, (0, 0, 0, 0), 8, 128)
+    assert s["base_over_non_shared"] == 0.25 and s["lr_share_of_base_shared"] == 0.0
+
+
+def test_cache_memory_matches_the_shared_decode_buffers():
+    # one layer of the shared-context decode batch: the K/V and LR buffers the call reads
+    # are the PreLRShared cache of its 16 contexts
+    p = workloads.decode_shared_batch()
+    m = accounting.cache_memory(16384, p.ranks, p.n_kv_heads, p.head_dim, n_layers=1)
+    kv_alloc = p.kv_rows * p.n_kv_heads * p.head_dim * 2 * 2
+    lr_alloc = sum(p.kv_rows * r * 2 for r in p.ranks)
+    assert kv_alloc == 16 * m["full_shared"]
+    assert kv_alloc + lr_alloc == 16 * m["pre_lr_shared"]
+
+
 def test_shared_rows_count_once():
     # two requests reading the same base rows: K/V bytes counted once, LR rows per request
     p = workloads.custom("s", "bf16", 8, 2, 64, (16,), [4, 4], [100, 100], [0, 0], seed=1,
