@@ -15,6 +15,7 @@ flushed between calls of the HBM-bound ones):
   decode_shared  16 contexts x 16384 keys, each read by all 4 agents (rank 16):
               64 requests whose K/V tiles are streamed once per context (HBM GB/s,
               shared rows counted once), also timed with grouping switched off
+  append      decode-step LR append: 64 new tokens x 4096 into 4 rank-16 caches (HBM GB/s)
   precompute  L = X·[A_1..A_3], X [32768, 4096], ranks 3 x 64              (HBM GB/s)
   longctx     512 queries over 32768 keys, rank 64, L from the precompute   (TFLOP/s)
   mixed       (--mixed) 32 layers of a 32-request batch, ranks 8/16/32/64   (roofline time)
@@ -232,6 +233,27 @@ def bench_decode_shared(steps, warmup, flush):
             "roofline": roof(gbs, accounting.PEAK_HBM_GBS, "GB/s", "hbm", traffic_bytes(prob.name))}
 
 
+def bench_append(steps, warmup, flush):
+    import torch
+    from shared_rank_kv_amd import accounting, lra, workloads
+    p = workloads.decode_append()
+    X = p.X().cuda()
+    A_cat = torch.cat([p.A(a) for a in range(len(p.ranks))], 1).contiguous().cuda()
+    l_rows = 64 * 16384
+    Ls = [torch.zeros(l_rows, r, dtype=torch.bfloat16, device="cuda") for r in p.ranks]
+    rows = np.arange(64) * 16384 + 16383
+    fn = lra.prepare_append_lr(X, A_cat, p.ranks, Ls, rows)
+    per, _ = time_calls(fn, steps, warmup, flush)
+    flop, nbytes = accounting.append_work(p)
+    del Ls
+    ms = float(np.median(per))
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": p.name, "value": round(gbs, 1), "unit": "GB/s",
+            "us_per_call": round(ms * 1e3, 2), "us_min": round(float(per.min()) * 1e3, 2),
+            "bytes": nbytes, "flop": flop,
+            "roofline": roof(gbs, accounting.PEAK_HBM_GBS, "GB/s", "hbm", traffic_bytes(p.name))}
+
+
 def bench_longctx(steps, warmup, flush):
     import torch
     from shared_rank_kv_amd import accounting, lra, workloads
@@ -400,6 +422,8 @@ def run_only(args):
         return bench_decode(args.steps, args.warmup, Flusher())
     if args.only == "decode_shared":
         return bench_decode_shared(args.steps, args.warmup, Flusher())
+    if args.only == "append":
+        return bench_append(args.steps, args.warmup, Flusher())
     if args.only == "longctx":
         pre, lc = bench_longctx(args.steps, args.warmup, Flusher())
         return {"precompute": pre, "longctx_prefill": lc}
@@ -412,8 +436,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--mixed", action="store_true", help="also time the 32-layer mixed batch")
-    ap.add_argument("--only", choices=["prefill", "decode", "decode_shared", "longctx", "mixed",
-                                       "copy"],
+    ap.add_argument("--only", choices=["prefill", "decode", "decode_shared", "append", "longctx",
+                                       "mixed", "copy"],
                     help="time one workload only (for profiling); prints its JSON object. "
                          "'copy' times a 1 GiB device copy, the reference for HBM counters")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -460,6 +484,8 @@ def main():
         out["decode"] = bench_decode(args.steps, args.warmup, flush)
         log("[bench] shared-context decode")
         out["decode_shared"] = bench_decode_shared(args.steps, args.warmup, flush)
+        log("[bench] decode-step LR append")
+        out["append"] = bench_append(args.steps, args.warmup, flush)
         log("[bench] precompute + long-context prefill")
         out["precompute"], out["longctx_prefill"] = bench_longctx(args.steps, args.warmup, flush)
         del flush

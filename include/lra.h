@@ -95,6 +95,33 @@ int lra_precompute_lr(int dtype, int64_t T, int64_t d_model,
                       void* stream);
 
 /*
+ * lra_append_lr -- decode-step append to the LR caches.  PreLRShared keeps every agent's
+ * LR cache over the shared context (PReCache abstract; LRAgent summary, section 2), so when
+ * new tokens are generated every agent's cache gains their rows, and no agent needs an LR
+ * prefill when it takes over:
+ *
+ *     L_a[rows[b], :] = X[b, :] · A_cat[:, off_a : off_a + r_a]
+ *
+ * for every new token b < batch and agent a < n_agents.
+ *   X        device [batch, d_model], row stride ldx: the new tokens' hidden states
+ *   A_cat, ranks, ldl: as for lra_precompute_lr
+ *   L_out    host [n_agents] array of device pointers; L_out[a] is [l_rows, r_a] with row
+ *            stride ldl[a]
+ *   rows     host [batch]: the cache row of token b, distinct, in [0, l_rows)
+ * Only the rows listed are written.  Same requirements as lra_precompute_lr, and batch <=
+ * LRA_MAX_BATCH; duplicate or out-of-range rows are LRA_ERR_INVALID.  The base K/V rows of
+ * the new tokens come from the model's own projections and are appended by the caller.
+ * batch == 0 is a no-op.
+ */
+int lra_append_lr(int dtype, int32_t batch, int64_t d_model,
+                  const void* X, int64_t ldx,
+                  const void* A_cat, int64_t lda,
+                  int32_t n_agents, const int32_t* ranks,
+                  void* const* L_out, const int64_t* ldl,
+                  const int32_t* rows, int64_t l_rows,
+                  void* stream);
+
+/*
  * lra_attn_prefill -- Flash-LoRA-Attention over a batch of requests (LRAgent summary,
  * section 3).  Request b:
  *   query rows  [q_start[b], q_start[b] + q_len[b])  of Q and O,

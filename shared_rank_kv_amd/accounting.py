@@ -81,6 +81,12 @@ def precompute_work(p):
     return flop, (p.T * p.d_model + p.d_model * R + p.T * R) * e
 
 
+def append_work(p):
+    """(flop, bytes) of one lra_append_lr call: the new tokens' rows of X, A_cat, and one
+    output row per token and agent (the precompute's counting rule on T new tokens)."""
+    return precompute_work(p)
+
+
 # ---------------------------------------------------------------------------------------
 # KV-cache memory of the sharing schemes (LRAgent summary, section 2; PReCache abstract)
 # ---------------------------------------------------------------------------------------

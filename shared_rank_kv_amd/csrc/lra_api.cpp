@@ -397,6 +397,73 @@ int run_attention(const AttnShape& s, bool decode, const Requests& rq, const voi
   return ok();
 }
 
+// Arguments shared by the LR precompute and the decode-step append (T rows of X), filled
+// into `a` on success; *R_out receives the sum of ranks.
+int check_lr_args(int dtype, int64_t T, int64_t d_model, const void* X, int64_t ldx,
+                  const void* A_cat, int64_t lda, int32_t n_agents, const int32_t* ranks,
+                  void* const* L_out, const int64_t* ldl, lra::PrecomputeArgs* a,
+                  int64_t* R_out) {
+  if (dtype != LRA_DTYPE_F32 && dtype != LRA_DTYPE_BF16)
+    return fail(LRA_ERR_INVALID, "dtype %d is neither LRA_DTYPE_F32 nor LRA_DTYPE_BF16", dtype);
+  if (T < 0 || d_model <= 0) return fail(LRA_ERR_INVALID, "T %lld < 0 or d_model %lld <= 0",
+                                         (long long)T, (long long)d_model);
+  if (n_agents <= 0) return fail(LRA_ERR_INVALID, "n_agents %d <= 0", n_agents);
+  if (n_agents > LRA_MAX_AGENTS)
+    return fail(LRA_ERR_UNSUPPORTED, "n_agents %d > LRA_MAX_AGENTS (%d)", n_agents, LRA_MAX_AGENTS);
+  if (!ranks || !L_out || !ldl) return fail(LRA_ERR_INVALID, "ranks, L_out, ldl must be non-null");
+  int64_t R = 0;
+  for (int i = 0; i < n_agents; ++i) {
+    if (ranks[i] < 0) return fail(LRA_ERR_INVALID, "ranks[%d] = %d < 0", i, ranks[i]);
+    if (ranks[i] > LRA_MAX_RANK || ranks[i] % 8 != 0)
+      return fail(LRA_ERR_UNSUPPORTED, "ranks[%d] = %d: ranks must be multiples of 8 up to %d", i,
+                  ranks[i], LRA_MAX_RANK);
+    if (ranks[i] > 0) {
+      if (!L_out[i]) return fail(LRA_ERR_INVALID, "L_out[%d] is null", i);
+      if (ldl[i] < ranks[i]) return fail(LRA_ERR_INVALID, "ldl[%d] < ranks[%d]", i, i);
+      if (!aligned(L_out[i], 4)) return fail(LRA_ERR_INVALID, "L_out[%d] not 4-byte aligned", i);
+    }
+    R += ranks[i];
+  }
+  if (d_model % 8 != 0) return fail(LRA_ERR_UNSUPPORTED, "d_model %lld %% 8 != 0", (long long)d_model);
+  if (dtype == LRA_DTYPE_BF16 && d_model % 64 != 0)
+    return fail(LRA_ERR_UNSUPPORTED, "bf16 d_model %lld %% 64 != 0", (long long)d_model);
+  if (ldx < d_model || ldx % 8 != 0)
+    return fail(LRA_ERR_INVALID, "ldx %lld must be >= d_model and a multiple of 8", (long long)ldx);
+  if (lda < R) return fail(LRA_ERR_INVALID, "lda %lld < sum of ranks %lld", (long long)lda,
+                           (long long)R);
+  *R_out = R;
+  if (T == 0 || R == 0) return LRA_OK;
+  if (!X || !A_cat) return fail(LRA_ERR_INVALID, "X and A_cat must be non-null");
+  if (!aligned(X, 16) || !aligned(A_cat, dtype == LRA_DTYPE_BF16 ? 16 : 4))
+    return fail(LRA_ERR_INVALID, "X must be 16-byte aligned, A_cat %d-byte aligned",
+                dtype == LRA_DTYPE_BF16 ? 16 : 4);
+  if (dtype == LRA_DTYPE_BF16 && (lda % 8 != 0))
+    return fail(LRA_ERR_INVALID, "lda %lld must be a multiple of 8 for bf16", (long long)lda);
+  if (R > 256) return fail(LRA_ERR_UNSUPPORTED, "sum of ranks %lld > 256", (long long)R);
+  // the bf16 kernels address 64 rows of X, or all of A_cat, with 32-bit offsets
+  if (dtype == LRA_DTYPE_BF16 && (ldx >= (1 << 24) || d_model * lda * 2 >= ((int64_t)1 << 31)))
+    return fail(LRA_ERR_UNSUPPORTED, "bf16 ldx %lld must be below 2^24 and A_cat below 2 GiB",
+                (long long)ldx);
+  std::memset(a, 0, sizeof(*a));
+  a->X = X;
+  a->A = A_cat;
+  a->T = T;
+  a->d_model = d_model;
+  a->ldx = ldx;
+  a->lda = lda;
+  a->R = (int)R;
+  a->n_agents = n_agents;
+  int32_t off = 0;
+  for (int i = 0; i < n_agents; ++i) {
+    a->Lout[i] = L_out[i];
+    a->ldl[i] = ldl[i];
+    a->col_start[i] = off;
+    off += ranks[i];
+  }
+  a->col_start[n_agents] = off;
+  return LRA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -471,67 +538,53 @@ int lra_attn_decode(int dtype, int32_t batch, int32_t n_q_heads, int32_t n_kv_he
 int lra_precompute_lr(int dtype, int64_t T, int64_t d_model, const void* X, int64_t ldx,
                       const void* A_cat, int64_t lda, int32_t n_agents, const int32_t* ranks,
                       void* const* L_out, const int64_t* ldl, void* stream) {
-  if (dtype != LRA_DTYPE_F32 && dtype != LRA_DTYPE_BF16)
-    return fail(LRA_ERR_INVALID, "dtype %d is neither LRA_DTYPE_F32 nor LRA_DTYPE_BF16", dtype);
-  if (T < 0 || d_model <= 0) return fail(LRA_ERR_INVALID, "T %lld < 0 or d_model %lld <= 0",
-                                         (long long)T, (long long)d_model);
-  if (n_agents <= 0) return fail(LRA_ERR_INVALID, "n_agents %d <= 0", n_agents);
-  if (n_agents > LRA_MAX_AGENTS)
-    return fail(LRA_ERR_UNSUPPORTED, "n_agents %d > LRA_MAX_AGENTS (%d)", n_agents, LRA_MAX_AGENTS);
-  if (!ranks || !L_out || !ldl) return fail(LRA_ERR_INVALID, "ranks, L_out, ldl must be non-null");
-  int64_t R = 0;
-  for (int a = 0; a < n_agents; ++a) {
-    if (ranks[a] < 0) return fail(LRA_ERR_INVALID, "ranks[%d] = %d < 0", a, ranks[a]);
-    if (ranks[a] > LRA_MAX_RANK || ranks[a] % 8 != 0)
-      return fail(LRA_ERR_UNSUPPORTED, "ranks[%d] = %d: ranks must be multiples of 8 up to %d", a,
-                  ranks[a], LRA_MAX_RANK);
-    if (ranks[a] > 0) {
-      if (!L_out[a]) return fail(LRA_ERR_INVALID, "L_out[%d] is null", a);
-      if (ldl[a] < ranks[a]) return fail(LRA_ERR_INVALID, "ldl[%d] < ranks[%d]", a, a);
-      if (!aligned(L_out[a], 4)) return fail(LRA_ERR_INVALID, "L_out[%d] not 4-byte aligned", a);
-    }
-    R += ranks[a];
-  }
-  if (d_model % 8 != 0) return fail(LRA_ERR_UNSUPPORTED, "d_model %lld %% 8 != 0", (long long)d_model);
-  if (dtype == LRA_DTYPE_BF16 && d_model % 64 != 0)
-    return fail(LRA_ERR_UNSUPPORTED, "bf16 d_model %lld %% 64 != 0", (long long)d_model);
-  if (ldx < d_model || ldx % 8 != 0)
-    return fail(LRA_ERR_INVALID, "ldx %lld must be >= d_model and a multiple of 8", (long long)ldx);
-  if (lda < R) return fail(LRA_ERR_INVALID, "lda %lld < sum of ranks %lld", (long long)lda,
-                           (long long)R);
-  if (T == 0 || R == 0) return ok();
-  if (!X || !A_cat) return fail(LRA_ERR_INVALID, "X and A_cat must be non-null");
-  if (!aligned(X, 16) || !aligned(A_cat, dtype == LRA_DTYPE_BF16 ? 16 : 4))
-    return fail(LRA_ERR_INVALID, "X must be 16-byte aligned, A_cat %d-byte aligned",
-                dtype == LRA_DTYPE_BF16 ? 16 : 4);
-  if (dtype == LRA_DTYPE_BF16 && (lda % 8 != 0))
-    return fail(LRA_ERR_INVALID, "lda %lld must be a multiple of 8 for bf16", (long long)lda);
-  if (R > 256) return fail(LRA_ERR_UNSUPPORTED, "sum of ranks %lld > 256", (long long)R);
-  // the bf16 kernel addresses 64 rows of X, or a 64-row chunk of A_cat, with 32-bit offsets
-  if (dtype == LRA_DTYPE_BF16 && (ldx >= (1 << 24) || lda >= (1 << 24)))
-    return fail(LRA_ERR_UNSUPPORTED, "bf16 ldx %lld / lda %lld must be below 2^24",
-                (long long)ldx, (long long)lda);
   lra::PrecomputeArgs a;
-  std::memset(&a, 0, sizeof(a));
-  a.X = X;
-  a.A = A_cat;
-  a.T = T;
-  a.d_model = d_model;
-  a.ldx = ldx;
-  a.lda = lda;
-  a.R = (int)R;
-  a.n_agents = n_agents;
-  int32_t off = 0;
-  for (int i = 0; i < n_agents; ++i) {
-    a.Lout[i] = L_out[i];
-    a.ldl[i] = ldl[i];
-    a.col_start[i] = off;
-    off += ranks[i];
-  }
-  a.col_start[n_agents] = off;
+  int64_t R = 0;
+  int rc = check_lr_args(dtype, T, d_model, X, ldx, A_cat, lda, n_agents, ranks, L_out, ldl,
+                         &a, &R);
+  if (rc != LRA_OK) return rc;
+  if (T == 0 || R == 0) return ok();
   hipError_t e = dtype == LRA_DTYPE_BF16 ? lra::launch_precompute_bf16(a, (hipStream_t)stream)
                                          : lra::launch_precompute_f32(a, (hipStream_t)stream);
   if (e != hipSuccess) return fail(LRA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int lra_append_lr(int dtype, int32_t batch, int64_t d_model, const void* X, int64_t ldx,
+                  const void* A_cat, int64_t lda, int32_t n_agents, const int32_t* ranks,
+                  void* const* L_out, const int64_t* ldl, const int32_t* rows, int64_t l_rows,
+                  void* stream) {
+  if (batch < 0) return fail(LRA_ERR_INVALID, "batch %d < 0", batch);
+  if (batch > LRA_MAX_BATCH)
+    return fail(LRA_ERR_UNSUPPORTED, "batch %d > LRA_MAX_BATCH (%d)", batch, LRA_MAX_BATCH);
+  lra::AppendArgs a;
+  std::memset(&a, 0, sizeof(a));
+  int64_t R = 0;
+  int rc = check_lr_args(dtype, batch, d_model, X, ldx, A_cat, lda, n_agents, ranks, L_out, ldl,
+                         &a.p, &R);
+  if (rc != LRA_OK) return rc;
+  if (batch == 0) return ok();
+  if (!rows) return fail(LRA_ERR_INVALID, "rows must be a non-null host array");
+  std::vector<int32_t> sorted(rows, rows + batch);
+  std::sort(sorted.begin(), sorted.end());
+  for (int b = 0; b < batch; ++b) {
+    if (sorted[b] < 0 || sorted[b] >= l_rows)
+      return fail(LRA_ERR_INVALID, "rows: %d outside [0, %lld)", sorted[b], (long long)l_rows);
+    if (b > 0 && sorted[b] == sorted[b - 1])
+      return fail(LRA_ERR_INVALID, "rows: row %d appears twice", sorted[b]);
+  }
+  if (R == 0) return ok();
+  const char* Xb = static_cast<const char*>(X);
+  const int64_t esz = dtype == LRA_DTYPE_BF16 ? 2 : 4;
+  for (int b0 = 0; b0 < batch; b0 += lra::kAppendRows) {
+    const int n = std::min(batch - b0, lra::kAppendRows);
+    a.p.X = Xb + (int64_t)b0 * ldx * esz;
+    a.p.T = n;
+    for (int i = 0; i < n; ++i) a.rows[i] = rows[b0 + i];
+    hipError_t e = dtype == LRA_DTYPE_BF16 ? lra::launch_append_bf16(a, (hipStream_t)stream)
+                                           : lra::launch_append_f32(a, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(LRA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  }
   return ok();
 }
 

@@ -80,6 +80,14 @@ struct PrecomputeArgs {
   int32_t col_start[kMaxAgents + 1];
 };
 
+// Decode-step append: the LR rows of up to kAppendRows new tokens per launch.  Token t of
+// the launch goes to row rows[t] of every agent's cache.
+constexpr int kAppendRows = 256;
+struct AppendArgs {
+  PrecomputeArgs p;    // X holds the launch's tokens (T of them), A_cat, the agents' caches
+  int32_t rows[kAppendRows];
+};
+
 // Launchers (return the HIP status of the launch).
 hipError_t launch_prefill_bf16(const AttnArgs& a, int head_dim, int max_rank, int n_grid,
                                hipStream_t s);
@@ -91,5 +99,7 @@ hipError_t launch_combine_bf16(const AttnArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgs& a, int head_dim, int n_blocks, hipStream_t s);
 hipError_t launch_precompute_bf16(const PrecomputeArgs& a, hipStream_t s);
 hipError_t launch_precompute_f32(const PrecomputeArgs& a, hipStream_t s);
+hipError_t launch_append_bf16(const AppendArgs& a, hipStream_t s);
+hipError_t launch_append_f32(const AppendArgs& a, hipStream_t s);
 
 }  // namespace lra

@@ -313,6 +313,113 @@ __global__ __launch_bounds__(256) void lr_precompute_f32(const PrecomputeArgs ar
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// Decode-step append: the LR rows of a few new tokens, L_a[rows[t]] = x_t·A_a for every
+// agent (the LR caches of PreLRShared kept current as tokens are generated).  The product
+// is tiny in tokens and long in d_model, so a workgroup owns 16 tokens x 16 columns and its
+// sixteen waves split d_model (32-value chunks dealt round-robin); the waves' sums meet in
+// LDS and are added in a fixed order, so results are deterministic and need no workspace.
+// The operands are those of the precompute: the X rows are the B operand (straight from
+// memory), each [32 x 16] A_cat block passes through LDS, rows permuted (a_k) for the
+// transposing read.  A wave issues the loads of a round of eight chunks together, waits
+// once, stores the round's eight blocks and then runs its MFMAs on four accumulators, so a
+// round costs one memory latency (d_model 4096 is one round).
+constexpr int kAppendWaves = 16;
+constexpr int kAppendRound = 8;               // chunks per wave per round
+
+__global__ __launch_bounds__(64 * kAppendWaves) void lr_append_bf16(const AppendArgs args) {
+  const AppendArgs* AA = (const AppendArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+  const PrecomputeArgs* P = &AA->p;
+  __shared__ __attribute__((aligned(16))) char tiles[kAppendWaves][kAppendRound][1024];
+  __shared__ float part[kAppendWaves][16][17];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = lane >> 4, col = lane & 15;
+  const int cb = blockIdx.x, tb = blockIdx.y;
+  const int64_t T = P->T, ldx = P->ldx, lda = P->lda;
+  const int R = P->R;
+  const int nk = (int)(P->d_model / 32);
+
+  // X: lane (grp, col) holds token 16 tb + col, d_model values 32 j + 8 grp .. + 8
+  const int64_t t0 = (int64_t)tb * 16;
+  const int64_t left = T - t0;
+  const int x_rows = left <= 0 ? 0 : (left < 16 ? (int)left : 16);
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc((const char*)P->X + t0 * ldx * 2,
+                                              (int)(x_rows * ldx * 2));
+  const int xoff = (int)(col * ldx * 2) + grp * 16;
+  // A_cat block of chunk j: lane l loads 8 columns (16 cb + 8 (l & 1) ..) of A_cat row
+  // 32 j + a_k(l / 2), which the LDS block keeps at row l / 2: offset 16 l
+  const int c8 = cb * 16 + 8 * (lane & 1);
+  const __amdgpu_buffer_rsrc_t ar = make_rsrc(P->A, (int)(P->d_model * lda * 2));
+  const int aoff = c8 < R ? (int)((a_k(lane >> 1) * lda + c8) * 2) : kOutOfRange;
+  const int a_chunk = (int)(32 * lda * 2);      // bytes of 32 A_cat rows
+  // transposing read: lane (grp, e, q) points at block row 4 grp + e (then + 16), columns
+  // 4 q .. + 4, and receives column col, d_model values 8 grp .. + 8 of the chunk
+  const int toff = (4 * grp + (col >> 2)) * 32 + (col & 3) * 8;
+
+  const int my = nk > wave ? (nk - wave + kAppendWaves - 1) / kAppendWaves : 0;
+  f32x4 acc[4] = {f32x4{}, f32x4{}, f32x4{}, f32x4{}};
+  for (int r0 = 0; r0 < my; r0 += kAppendRound) {
+    u32x4 xq[kAppendRound], aq[kAppendRound];
+#pragma unroll
+    for (int i = 0; i < kAppendRound; ++i) {
+      // chunks past this wave's last read zeros (soffset past every record)
+      const int j = wave + (r0 + i) * kAppendWaves;
+      const bool ok = r0 + i < my;
+      xq[i] = load_b128(xr, xoff, __builtin_amdgcn_readfirstlane(ok ? j * 64 : kOutOfRange));
+      aq[i] = load_b128(ar, aoff, __builtin_amdgcn_readfirstlane(ok ? j * a_chunk : kOutOfRange));
+    }
+    // the previous round's reads of these blocks precede the writes in program order, and
+    // the LDS executes one wave's operations in order
+#pragma unroll
+    for (int i = 0; i < kAppendRound; ++i)
+      *(LDS u32x4*)((LDS char*)tiles[wave][i] + lane * 16) = aq[i];
+#pragma unroll
+    for (int i = 0; i < kAppendRound; ++i) {
+      const LDS char* t = (const LDS char*)tiles[wave][i];
+      const bf16x8 aop = join(tr_read(t + toff), tr_read(t + toff + 16 * 32));
+      acc[i & 3] = mfma16(aop, __builtin_bit_cast(bf16x8, xq[i]), acc[i & 3]);
+    }
+  }
+  // acc register j of lane (grp, col): column 16 cb + 4 grp + j, token 16 tb + col
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    part[wave][4 * grp + j][col] = (acc[0][j] + acc[1][j]) + (acc[2][j] + acc[3][j]);
+  __syncthreads();
+  if (tid < 256) {
+    const int cl = tid & 15, tl = tid >> 4;           // column, token of this thread
+    const int c = cb * 16 + cl;
+    const int64_t t = t0 + tl;
+    if (c < R && t < T) {
+      float v = 0.f;
+#pragma unroll
+      for (int w = 0; w < kAppendWaves; ++w) v += part[w][cl][tl];
+      int a = 0;
+      while (a + 1 < P->n_agents && P->col_start[a + 1] <= c) ++a;
+      bf16* Lp = (bf16*)P->Lout[a];
+      Lp[(int64_t)AA->rows[t] * P->ldl[a] + (c - P->col_start[a])] = (bf16)v;
+    }
+  }
+}
+
+// fp32 append: one thread per (token, column), a plain fp32 dot product over d_model.
+__global__ __launch_bounds__(256) void lr_append_f32(const AppendArgs args) {
+  const AppendArgs* AA = (const AppendArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+  const PrecomputeArgs* P = &AA->p;
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= P->T * P->R) return;
+  const int64_t t = e / P->R;
+  const int c = (int)(e % P->R);
+  const float* x = (const float*)P->X + t * P->ldx;
+  const float* A = (const float*)P->A + c;
+  float v = 0.f;
+  for (int64_t k = 0; k < P->d_model; ++k) v = fmaf(x[k], A[k * P->lda], v);
+  int a = 0;
+  while (a + 1 < P->n_agents && P->col_start[a + 1] <= c) ++a;
+  float* Lp = (float*)P->Lout[a];
+  Lp[(int64_t)AA->rows[t] * P->ldl[a] + (c - P->col_start[a])] = v;
+}
+
 }  // namespace
 
 hipError_t launch_precompute_bf16(const PrecomputeArgs& a, hipStream_t s) {
@@ -333,6 +440,18 @@ hipError_t launch_precompute_f32(const PrecomputeArgs& a, hipStream_t s) {
   const int rt = (int)((a.T + 63) / 64);
   const int ct = (a.R + 63) / 64;
   hipLaunchKernelGGL(lr_precompute_f32, dim3(rt, ct), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_append_bf16(const AppendArgs& a, hipStream_t s) {
+  const dim3 grid((a.p.R + 15) / 16, (unsigned)((a.p.T + 15) / 16));
+  hipLaunchKernelGGL(lr_append_bf16, grid, dim3(64 * kAppendWaves), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_append_f32(const AppendArgs& a, hipStream_t s) {
+  const int64_t n = a.p.T * a.p.R;
+  hipLaunchKernelGGL(lr_append_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblra.so")
 
 LRA_OK, LRA_ERR_INVALID, LRA_ERR_UNSUPPORTED, LRA_ERR_WORKSPACE, LRA_ERR_HIP = range(5)
 LRA_DTYPE_F32, LRA_DTYPE_BF16 = 0, 1
-SYMBOLS = ("lra_precompute_lr", "lra_attn_prefill", "lra_attn_decode",
+SYMBOLS = ("lra_precompute_lr", "lra_append_lr", "lra_attn_prefill", "lra_attn_decode",
            "lra_attn_workspace_bytes", "lra_last_error")
 
 _c_i32p = ctypes.POINTER(ctypes.c_int32)
@@ -40,6 +40,9 @@ def _load():
     I, L, P, S = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
     lib.lra_precompute_lr.argtypes = [ctypes.c_int, L, L, P, L, P, L, I, _c_i32p, _c_vpp, _c_i64p, P]
     lib.lra_precompute_lr.restype = ctypes.c_int
+    lib.lra_append_lr.argtypes = [ctypes.c_int, I, L, P, L, P, L, I, _c_i32p, _c_vpp, _c_i64p,
+                                  _c_i32p, L, P]
+    lib.lra_append_lr.restype = ctypes.c_int
     lib.lra_attn_prefill.argtypes = [ctypes.c_int, I, I, I, I, _c_i32p, _c_i32p, _c_i32p, _c_i32p,
                                      _c_i32p, P, L, P, P, L, I, _c_i32p, _c_vpp, _c_i64p, _c_vpp,
                                      P, P, S, P]
@@ -165,6 +168,30 @@ def prepare_precompute_lr(X, A_cat, ranks, L_out):
 def lra_precompute_lr(X, A_cat, ranks, L_out, stream=None):
     """L_out[a] <- X · A_cat[:, off_a:off_a + ranks[a]] (PreLRShared precompute)."""
     return prepare_precompute_lr(X, A_cat, ranks, L_out)(stream)
+
+
+def prepare_append_lr(X, A_cat, ranks, L_out, rows):
+    """Prepared lra_append_lr: L_out[a][rows[b]] <- X[b] · A_cat[:, off_a:off_a + ranks[a]].
+
+    X [batch, d_model] (the new tokens), A_cat [d_model, sum(ranks)], L_out: list of
+    [l_rows, r_a] GPU tensors sharing l_rows (row stride = stride(0)), rows: batch
+    distinct cache rows.
+    """
+    _dtype(X)
+    assert X.dim() == 2 and A_cat.dim() == 2 and X.stride(1) == 1 and A_cat.stride(1) == 1
+    rk, rkp = _i32(ranks)
+    pk, ptrs = _ptrs(L_out)
+    ld, ldp = _i64([t.stride(0) if t is not None else 0 for t in L_out])
+    rw, rwp = _i32(rows)
+    l_rows = max([t.shape[0] for t in L_out if t is not None] + [0])
+    args = (_dtype(X), X.shape[0], X.shape[1], X.data_ptr(), X.stride(0), A_cat.data_ptr(),
+            A_cat.stride(0), len(rk), rkp, ptrs, ldp, rwp, l_rows, None)
+    return Prepared(lib.lra_append_lr, args, (X, A_cat, L_out, rk, pk, ld, rw), L_out, 13)
+
+
+def lra_append_lr(X, A_cat, ranks, L_out, rows, stream=None):
+    """L_out[a][rows[b]] <- X[b] · A_cat[:, off_a:off_a + ranks[a]] (decode-step LR append)."""
+    return prepare_append_lr(X, A_cat, ranks, L_out, rows)(stream)
 
 
 def prepare_attn_prefill(Q, K_base, V_base, L, B, q_start, q_len, k_start, k_len, agent_idx,

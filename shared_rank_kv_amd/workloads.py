@@ -184,6 +184,14 @@ def decode_shared_batch():
                          [(16384, [0, 1, 2, 3])] * 16, seed=SEED_BASE + 5)
 
 
+def decode_append():
+    """Decode-step LR append for the decode batch: the 64 requests' new tokens (X [64, 4096]
+    ~ N(0,1)) into the four rank-16 agents' LR caches (A_a [4096, 16] ~ N(0, 1/4096)); token
+    b lands on row 16384 b + 16383 of every agent's cache [64 x 16384, 16]."""
+    return PrecomputeProblem(name="lr-append-64x4096-4x16", dtype="bf16", T=64, d_model=4096,
+                             ranks=(16, 16, 16, 16), seed=SEED_BASE + 6)
+
+
 def longctx_precompute():
     """LR precompute for the 32768-token context: X [32768, 4096] ~ N(0,1), three agents'
     A_a [4096, 64] ~ N(0, 1/4096)."""

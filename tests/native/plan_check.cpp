@@ -26,6 +26,8 @@ hipError_t launch_combine_bf16(const AttnArgs& a, int, hipStream_t) { g_recs.pus
 hipError_t launch_attn_f32(const AttnArgs& a, int, int, hipStream_t) { g_recs.push_back({a, 4}); return hipSuccess; }
 hipError_t launch_precompute_bf16(const PrecomputeArgs&, hipStream_t) { return hipSuccess; }
 hipError_t launch_precompute_f32(const PrecomputeArgs&, hipStream_t) { return hipSuccess; }
+hipError_t launch_append_bf16(const AppendArgs&, hipStream_t) { return hipSuccess; }
+hipError_t launch_append_f32(const AppendArgs&, hipStream_t) { return hipSuccess; }
 }
 
 static int check(int batch, int Hq, int Hkv, const std::vector<int>& ks, const std::vector<int>& kl,

@@ -195,6 +195,46 @@ def test_precompute_empty_is_noop():
     assert _precompute(T=0, X=None, A=None)[0] == lra.LRA_OK
 
 
+def _append(rows=(5, 0, 9), l_rows=10, batch=None, **kw):
+    d = dict(dtype=lra.LRA_DTYPE_BF16, dm=64, X=FAKE, ldx=64, A=FAKE, lda=24, ranks=(8, 16),
+             L=(FAKE, FAKE + 4096), ldl=(8, 16))
+    d.update(kw)
+    batch = len(rows) if batch is None else batch
+    I = (ctypes.c_int32 * len(d["ranks"]))(*d["ranks"])
+    P = (ctypes.c_void_p * len(d["L"]))(*d["L"])
+    LD = (ctypes.c_int64 * len(d["ldl"]))(*d["ldl"])
+    RW = (ctypes.c_int32 * max(1, len(rows)))(*rows) if rows is not None else None
+    rc = lra.lib.lra_append_lr(d["dtype"], batch, d["dm"], d["X"], d["ldx"], d["A"], d["lda"],
+                               len(d["ranks"]), ctypes.cast(I, ctypes.POINTER(ctypes.c_int32)),
+                               ctypes.cast(P, ctypes.POINTER(ctypes.c_void_p)),
+                               ctypes.cast(LD, ctypes.POINTER(ctypes.c_int64)),
+                               ctypes.cast(RW, ctypes.POINTER(ctypes.c_int32)) if RW else None,
+                               l_rows, None)
+    return rc, lra.lra_last_error()
+
+
+@pytest.mark.parametrize("kw,code,frag", [
+    (dict(rows=(5, 5, 1)), lra.LRA_ERR_INVALID, "twice"),
+    (dict(rows=(5, 10)), lra.LRA_ERR_INVALID, "outside"),
+    (dict(rows=(-1,)), lra.LRA_ERR_INVALID, "outside"),
+    (dict(rows=None, batch=2), lra.LRA_ERR_INVALID, "rows"),
+    (dict(batch=-1, rows=()), lra.LRA_ERR_INVALID, "batch"),
+    (dict(batch=2000, rows=()), lra.LRA_ERR_UNSUPPORTED, "LRA_MAX_BATCH"),
+    (dict(dm=72, ldx=72), lra.LRA_ERR_UNSUPPORTED, "% 64"),
+    (dict(ranks=(8, 20)), lra.LRA_ERR_UNSUPPORTED, "multiples of 8"),
+    (dict(L=(FAKE, None)), lra.LRA_ERR_INVALID, "null"),
+    (dict(X=None), lra.LRA_ERR_INVALID, "non-null"),
+])
+def test_append_rejections(kw, code, frag):
+    rc, msg = _append(**kw)
+    assert rc == code, (rc, msg)
+    assert frag in msg, msg
+
+
+def test_append_empty_is_noop():
+    assert _append(rows=(), X=None, A=None)[0] == lra.LRA_OK
+
+
 def test_decode_rejections():
     I = lambda a: ctypes.cast((ctypes.c_int32 * len(a))(*a), ctypes.POINTER(ctypes.c_int32))  # noqa
     P = lambda a: ctypes.cast((ctypes.c_void_p * len(a))(*a), ctypes.POINTER(ctypes.c_void_p))  # noqa

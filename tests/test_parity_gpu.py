@@ -279,3 +279,42 @@ def test_precompute_into_rows_of_odd_stride():
     torch.cuda.synchronize()
     assert torch.equal(buf[:, 2:18], sep[0]) and torch.equal(buf[:, 18:50], sep[1])
     assert (buf[:, :2] == 0).all()
+
+
+# ---------------------------------------------------------------------------------------
+# Decode-step LR append
+# ---------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,batch,dm,ranks,l_rows", [
+    ("bf16", 64, 4096, (16, 16, 16, 16), 3000),   # a decode batch, four rank-16 agents
+    ("bf16", 37, 512, (64, 64, 64), 300),          # ragged token block, R = 192
+    ("bf16", 1, 128, (8,), 5),                     # one token, one column block
+    ("bf16", 300, 256, (0, 40, 24, 64, 64, 64), 700),   # two launches, R = 256, rank 0
+    ("f32", 20, 136, (8, 24), 50),
+])
+def test_append_lr(dtype, batch, dm, ranks, l_rows):
+    import oracle
+    from shared_rank_kv_amd import inputs, lra
+    p = workloads.PrecomputeProblem("append", dtype, batch, dm, ranks, seed=720 + batch)
+    X = p.X()
+    A = [p.A(a) for a in range(len(ranks))]
+    A_cat = torch.cat(A, dim=1).contiguous()
+    rows = np.random.default_rng(batch).choice(l_rows, size=batch, replace=False)
+    outs = [torch.full((l_rows, r), float("nan"), dtype=X.dtype, device="cuda") for r in ranks]
+    lra.lra_append_lr(X.cuda(), A_cat.cuda(), ranks, outs, rows)
+    torch.cuda.synchronize()
+    again = [o.clone() for o in outs]
+    lra.lra_append_lr(X.cuda(), A_cat.cuda(), ranks, again, rows)
+    torch.cuda.synchronize()
+    Xf = inputs.to_f64(X)
+    want = oracle.lr_precompute(Xf, [inputs.to_f64(a) for a in A])
+    others = np.setdiff1d(np.arange(l_rows), rows)
+    for a in range(len(ranks)):
+        got = outs[a].double().cpu().numpy()
+        bound = dm * 2.0 ** -23 * (np.abs(Xf) @ np.abs(inputs.to_f64(A[a])))
+        if dtype == "bf16":
+            bound = bound + 2.0 ** -8 * np.abs(want[a])
+        assert np.all(np.abs(got[rows] - want[a]) <= bound + 1e-30), f"agent {a}"
+        assert np.isnan(got[others]).all(), f"agent {a}: rows outside `rows` were written"
+        assert torch.equal(outs[a][rows], again[a][rows]), "repeat call not bitwise identical"
+

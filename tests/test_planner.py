@@ -19,11 +19,13 @@ def test_planner_units_and_launches(tmp_path):
     for src in (os.path.join(csrc, "lra_api.cpp"), os.path.join(ROOT, "tests", "native",
                                                                   "plan_check.cpp")):
         obj = str(tmp_path / (os.path.basename(src) + ".o"))
-        subprocess.run([HIPCC, *flags, "-c", src, "-o", obj], check=True, capture_output=True)
+        r = subprocess.run([HIPCC, *flags, "-c", src, "-o", obj], capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr
         objs.append(obj)
     exe = str(tmp_path / "plan_check")
-    subprocess.run([HIPCC, "--offload-arch=gfx950", *objs, "-o", exe], check=True,
-                   capture_output=True)
+    r = subprocess.run([HIPCC, "--offload-arch=gfx950", *objs, "-o", exe], capture_output=True,
+                       text=True)
+    assert r.returncode == 0, r.stderr
     r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "planner checks passed" in r.stdout
