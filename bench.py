@@ -32,6 +32,7 @@ import hashlib
 import json
 import os
 import platform
+import shutil
 import sys
 import time
 
@@ -63,6 +64,19 @@ class Flusher:
 
     def __call__(self):
         self.buf.sum()
+
+
+def settle(fn, seconds=0.5):
+    """Runs fn back to back for about `seconds` of wall time before anything is timed.  The
+    headline is the first workload a fresh process runs, and an idle GPU takes some
+    milliseconds of load to reach its working clock; the W warm-up steps alone (about 1 ms
+    of work) do not cover that."""
+    import torch
+    t_end = time.time() + seconds
+    while time.time() < t_end:
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
 
 
 def time_calls(fn, steps, warmup, flush=None):
@@ -103,13 +117,14 @@ def time_calls(fn, steps, warmup, flush=None):
 # what the same counter reads for a plain 1 GiB device copy); the per-kernel summaries and
 # the commands are under profiles/.  The figures describe the kernels built from sources
 # with this digest and are reported as null for any other sources.
-TRAFFIC_SOURCES_SHA256 = "6013db3b93d9433766d8dbef48897916a7f5158a2fba17152d5f8108d5c175a8"
+TRAFFIC_SOURCES_SHA256 = "56b731000996b9a6d11eed7afa1036f315693489984708529fc77794fce94758"
 TRAFFIC_BYTES = {
-    "llama8b-prefill-1024q-9216k-r16": 127036105,
-    "decode-64x16384-r16": 4419107254,
-    "decode-shared-16x4x16384-r16": 1161952109,
-    "lr-precompute-32768x4096-3x64": 293966016,
-    "longctx-prefill-512q-32768k-r64": 245418831,
+    "llama8b-prefill-1024q-9216k-r16": 127035600,
+    "decode-64x16384-r16": 4417532265,
+    "decode-shared-16x4x16384-r16": 1163159262,
+    "lr-precompute-32768x4096-3x64": 293967574,
+    "lr-append-64x4096-4x16": 6361086,
+    "longctx-prefill-512q-32768k-r64": 245418079,
 }
 
 
@@ -176,6 +191,7 @@ def bench_llama_prefill(steps, warmup):
     cpu, dev = upload(prob)
     ws = workspace_for(prob, False)
     fn = prefill_call(prob, dev, ws)
+    settle(fn)
     per, total = time_calls(fn, steps, warmup)
     flop, nbytes = accounting.attention_work(prob)
     return prob, cpu, dev, {"flop": flop, "bytes": nbytes, "per_ms": per, "total_ms": total}
@@ -399,7 +415,10 @@ def environment():
     env = {"device": props.name, "compute_units": props.multi_processor_count,
            "torch": torch.__version__, "hip": torch.version.hip}
     try:
-        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True,
+        # rocm-smi is a Python script: run it with this interpreter, so no launcher (env)
+        # sits between this process and the child
+        smi = os.path.realpath(shutil.which("rocm-smi"))
+        r = subprocess.run([sys.executable, smi, "--showclocks", "--json"], capture_output=True,
                            text=True, timeout=20)
         clk = json.loads(r.stdout)
         card = next(iter(clk.values()))
