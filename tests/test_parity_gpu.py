@@ -114,7 +114,10 @@ def test_bf16_split_invariance_and_determinism(monkeypatch):
     prob = workloads.custom("bf16-split", "bf16", 8, 2, 128, (32,), [90], [3000], [0], seed=630)
     cpu, dev = H.device_inputs(prob)
     outs = {}
-    for target in ("1", "64", "4096"):
+    # 90 queries x 4 heads per kv head = 2 row tiles per kv head, 4 workgroups unsplit:
+    # targets 8, 12 and 16 split the keys 2, 3 and 4 ways, 64 and 4096 split them 5 ways
+    # (47 key tiles / 8)
+    for target in ("1", "8", "12", "16", "64", "4096"):
         monkeypatch.setenv("LRA_PREFILL_TARGET_WG", target)
         outs[target] = H.run_prefill(prob, dev).float().cpu().numpy()
         again = H.run_prefill(prob, dev).float().cpu().numpy()
@@ -122,7 +125,7 @@ def test_bf16_split_invariance_and_determinism(monkeypatch):
     want = H.oracle_all(prob, cpu)
     for k, v in outs.items():
         H.assert_bf16_close(v, want, f"target {k}")
-    for k in ("64", "4096"):
+    for k in ("8", "12", "16", "64", "4096"):
         assert np.abs(outs[k] - outs["1"]).max() <= 4e-3
 
 
