@@ -528,13 +528,17 @@ __global__ __launch_bounds__(512, 1) void fla_prefill_bf16(const AttnArgs args) 
 // Merge the key-split states of one output row:
 //   M = max m_s, w_s = 2^(m_s - M),   O = Σ w_s·acc_s / Σ w_s·l_s
 // where acc_s = (P·V_base)_s + (P·L)_s·B_g already holds the up-projection (B is linear).
-// D/4 threads per row, each owning 4 consecutive output lanes.
-template <int D>
+// D/VPT threads per row, each owning VPT consecutive output lanes; the splits are merged
+// NB at a time with all of their loads in flight before the first is used.  The pass is
+// bound by load latency: many rows (a split prefill) take VPT = 16, so that a wave keeps
+// several KB of loads outstanding; few rows with many splits (decode) take VPT = 4 and
+// NB = 8, so that the launch still spreads over the CUs.
+template <int D, int VPT, int NB>
 __global__ __launch_bounds__(256) void fla_combine_bf16(const AttnArgs args) {
   const AttnArgs* A = (const AttnArgs*)__builtin_amdgcn_kernarg_segment_ptr();
-  constexpr int TPR = D / 4, RPB = 256 / TPR;
+  constexpr int TPR = D / VPT, RPB = 256 / TPR;
   const int row = blockIdx.x * RPB + threadIdx.x / TPR;
-  const int q4 = threadIdx.x % TPR;
+  const int c0 = (threadIdx.x % TPR) * VPT;
   const int b = find_combine_request(A, min(row, A->n_comb - 1));   // whole wave
   if (row >= A->n_comb) return;
   const ReqDesc& R = A->reqs[b];
@@ -544,41 +548,61 @@ __global__ __launch_bounds__(256) void fla_combine_bf16(const AttnArgs args) {
   const int S = R.n_split;
   const int64_t p0 = (int64_t)R.part_base + (int64_t)t * Hq + h;
   const int64_t pstride = (int64_t)R.q_len * Hq;
-  // splits are merged 8 at a time, with all 8 loads in flight before the first is used
   float M = kNegBig, l = 0.f;
-  f32x4 o = {};
-  for (int s0 = 0; s0 < S; s0 += 8) {
-    float2 ml[8];
-    f32x4 v[8];
+  f32x4 o[VPT / 4] = {};
+  for (int s0 = 0; s0 < S; s0 += NB) {
+    float2 ml[NB];
+    f32x4 v[NB][VPT / 4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < NB; ++i) {
       const int64_t pr = p0 + (int64_t)(s0 + i) * pstride;
       ml[i] = float2{kNegBig, 0.f};
-      v[i] = f32x4{};
+#pragma unroll
+      for (int k = 0; k < VPT / 4; ++k) v[i][k] = f32x4{};
       if (s0 + i < S) {
         ml[i] = *(const float2*)(A->ws_ml + pr * 2);
-        v[i] = *(const f32x4*)(A->ws_o + pr * D + q4 * 4);
+#pragma unroll
+        for (int k = 0; k < VPT / 4; ++k) v[i][k] = *(const f32x4*)(A->ws_o + pr * D + c0 + 4 * k);
       }
     }
     float Mc = M;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) Mc = fmaxf(Mc, ml[i].x);
+    for (int i = 0; i < NB; ++i) Mc = fmaxf(Mc, ml[i].x);
     const float sc = __builtin_amdgcn_exp2f(M - Mc);
     l *= sc;
-    o *= sc;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int k = 0; k < VPT / 4; ++k) o[k] *= sc;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
       const float w = __builtin_amdgcn_exp2f(ml[i].x - Mc);   // 0 for absent splits
       l += w * ml[i].y;
-      o += w * v[i];
+#pragma unroll
+      for (int k = 0; k < VPT / 4; ++k) o[k] += w * v[i][k];
     }
     M = Mc;
   }
   const float inv = 1.f / l;
-  bf16x4 ob;
+  bf16* orow = (bf16*)A->O + ((int64_t)(R.q_start + t) * Hq + h) * D + c0;
+  if constexpr (VPT % 8 == 0) {   // 16-byte stores
 #pragma unroll
-  for (int j2 = 0; j2 < 4; ++j2) ob[j2] = (bf16)(o[j2] * inv);
-  *(bf16x4*)((bf16*)A->O + ((int64_t)(R.q_start + t) * Hq + h) * D + q4 * 4) = ob;
+    for (int k = 0; k < VPT / 4; k += 2) {
+      bf16x8 ob;
+#pragma unroll
+      for (int j2 = 0; j2 < 4; ++j2) {
+        ob[j2] = (bf16)(o[k][j2] * inv);
+        ob[4 + j2] = (bf16)(o[k + 1][j2] * inv);
+      }
+      *(bf16x8*)(orow + 4 * k) = ob;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < VPT / 4; ++k) {
+      bf16x4 ob;
+#pragma unroll
+      for (int j2 = 0; j2 < 4; ++j2) ob[j2] = (bf16)(o[k][j2] * inv);
+      *(bf16x4*)(orow + 4 * k) = ob;
+    }
+  }
 }
 
 }  // namespace
@@ -602,12 +626,20 @@ hipError_t launch_prefill_bf16(const AttnArgs& a, int head_dim, int max_rank, in
 }
 
 hipError_t launch_combine_bf16(const AttnArgs& a, int head_dim, hipStream_t s) {
-  const int rpb = 256 / (head_dim / 4);
+  // 16 values per thread once that still gives at least 256 blocks
+  const bool wide = (int64_t)a.n_comb * (head_dim / 16) >= 256 * 256;
+  const int rpb = 256 / (head_dim / (wide ? 16 : 4));   // rows per block
   const int grid = (a.n_comb + rpb - 1) / rpb;
-  if (head_dim == 128)
-    hipLaunchKernelGGL(fla_combine_bf16<128>, dim3(grid), dim3(kThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL(fla_combine_bf16<64>, dim3(grid), dim3(kThreads), 0, s, a);
+#define LRA_COMBINE(D, VPT, NB) \
+  hipLaunchKernelGGL((fla_combine_bf16<D, VPT, NB>), dim3(grid), dim3(kThreads), 0, s, a)
+  if (head_dim == 128) {
+    if (wide) LRA_COMBINE(128, 16, 4);
+    else LRA_COMBINE(128, 4, 8);
+  } else {
+    if (wide) LRA_COMBINE(64, 16, 4);
+    else LRA_COMBINE(64, 4, 8);
+  }
+#undef LRA_COMBINE
   return hipGetLastError();
 }
 
