@@ -235,7 +235,10 @@ __global__ __launch_bounds__(512, 1) void fla_prefill_bf16(const AttnArgs args) 
   LDS char* const buf2 = (LDS char*)smem2;
 
   const int bid = blockIdx.x;
-  const int w = (bid & 7) * A->grid_per_xcd + (bid >> 3);
+  const int w = A->grid_per_xcd > 0
+                    ? (bid & 7) * A->grid_per_xcd + (bid >> 3)
+                    : ((bid >> 3) / kDealChunk) * (8 * kDealChunk) + (bid & 7) * kDealChunk +
+                          (bid >> 3) % kDealChunk;
   if (w >= A->n_work) return;
   const int b = find_request(A, w);
   const ReqDesc& R = A->reqs[b];

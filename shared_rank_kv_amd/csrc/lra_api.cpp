@@ -333,6 +333,24 @@ int run_attention(const AttnShape& s, bool decode, const Requests& rq, const voi
         for (int k = 0; k < unit_size[u]; ++k) p.n_split[i + k] = split_u[u];
     }
   }
+  // bf16 prefill with several requests: longest work items first (their keys per item,
+  // ceil(k_len / n_split)), so that the launch does not end on a few long workgroups; the
+  // kernel then deals the items round-robin over the XCDs (grid_per_xcd = 0).  The order
+  // of requests does not change any result.
+  const bool longest_first = !decode && s.dtype == LRA_DTYPE_BF16 && n > 1;
+  if (longest_first) {
+    std::vector<size_t> ord(n);
+    for (size_t i = 0; i < n; ++i) ord[i] = i;
+    auto keys = [&](size_t i) { return ceil_div(rq.k_len[p.active[i]], p.n_split[i]); };
+    std::stable_sort(ord.begin(), ord.end(), [&](size_t x, size_t y) { return keys(x) > keys(y); });
+    Plan q = p;
+    for (size_t i = 0; i < n; ++i) {
+      p.active[i] = q.active[ord[i]];
+      p.n_rt[i] = q.n_rt[ord[i]];
+      p.n_split[i] = q.n_split[ord[i]];
+      p.part_base[i] = q.part_base[ord[i]];
+    }
+  }
   const int heads_per_item = s.dtype == LRA_DTYPE_F32 ? s.Hq : s.Hkv;
   size_t c0 = 0, u0 = 0;
   while (c0 < n) {
@@ -375,8 +393,10 @@ int run_attention(const AttnShape& s, bool decode, const Requests& rq, const voi
     a.n_comb = (int)comb;
     hipError_t e;
     if (s.dtype == LRA_DTYPE_BF16) {
-      const int grid = (int)ceil_div(work, 8) * 8;
-      a.grid_per_xcd = grid / 8;
+      const bool dealt = longest_first && c1 - c0 > 1;
+      const int64_t round = dealt ? 8 * lra::kDealChunk : 8;
+      const int grid = (int)(ceil_div(work, round) * round);
+      a.grid_per_xcd = dealt ? 0 : grid / 8;
       int max_rank = 0;
       for (size_t i = c0; i < c1; ++i) max_rank = std::max(max_rank, ad.ranks[rq.agent[p.active[i]]]);
       if (!decode)

@@ -49,6 +49,10 @@ struct ReqDesc {
 // query heads share the 16 columns of one MFMA tile).
 constexpr int kMaxMembers = 4;
 
+// Consecutive work items per XCD turn in the longest-first prefill mapping (grid_per_xcd
+// == 0); the grid is then a multiple of 8 * kDealChunk.
+constexpr int kDealChunk = 4;
+
 struct AttnArgs {
   const void* Q;
   const void* K;
@@ -59,6 +63,11 @@ struct AttnArgs {
   int32_t Hq, Hkv, G;
   int32_t n_req;
   int32_t n_work;      // work items (workgroups that do work) in this launch
+  // Workgroup -> work item.  > 0: XCD-major, XCD x (blockIdx % 8) takes the contiguous
+  // items [x * grid_per_xcd, (x + 1) * grid_per_xcd), so the items of one kv head share
+  // that XCD's L2.  0 (bf16 prefill with several requests, sorted longest first): the items
+  // are dealt round-robin over the XCDs in chunks of kDealChunk, so every XCD starts on
+  // long items and ends on short ones.
   int32_t grid_per_xcd;
   int32_t n_comb;      // combine rows in this launch
   float scale_log2;    // log2(e) / sqrt(D)

@@ -16,14 +16,14 @@
 #include "lra.h"
 #include "lra_internal.h"
 
-struct Rec { lra::AttnArgs a; int kind; };   // 0 prefill, 1 decode, 2 decode shared, 3 combine, 4 f32
+struct Rec { lra::AttnArgs a; int kind; int grid; };   // 0 prefill, 1 decode, 2 decode shared, 3 combine, 4 f32
 static std::vector<Rec> g_recs;
 namespace lra {
-hipError_t launch_prefill_bf16(const AttnArgs& a, int, int, int, hipStream_t) { g_recs.push_back({a, 0}); return hipSuccess; }
-hipError_t launch_decode_bf16(const AttnArgs& a, int, int, int, hipStream_t) { g_recs.push_back({a, 1}); return hipSuccess; }
-hipError_t launch_decode_shared_bf16(const AttnArgs& a, int, int, int, hipStream_t) { g_recs.push_back({a, 2}); return hipSuccess; }
-hipError_t launch_combine_bf16(const AttnArgs& a, int, hipStream_t) { g_recs.push_back({a, 3}); return hipSuccess; }
-hipError_t launch_attn_f32(const AttnArgs& a, int, int, hipStream_t) { g_recs.push_back({a, 4}); return hipSuccess; }
+hipError_t launch_prefill_bf16(const AttnArgs& a, int, int, int grid, hipStream_t) { g_recs.push_back({a, 0, grid}); return hipSuccess; }
+hipError_t launch_decode_bf16(const AttnArgs& a, int, int, int, hipStream_t) { g_recs.push_back({a, 1, 0}); return hipSuccess; }
+hipError_t launch_decode_shared_bf16(const AttnArgs& a, int, int, int, hipStream_t) { g_recs.push_back({a, 2, 0}); return hipSuccess; }
+hipError_t launch_combine_bf16(const AttnArgs& a, int, hipStream_t) { g_recs.push_back({a, 3, 0}); return hipSuccess; }
+hipError_t launch_attn_f32(const AttnArgs& a, int, int, hipStream_t) { g_recs.push_back({a, 4, 0}); return hipSuccess; }
 hipError_t launch_precompute_bf16(const PrecomputeArgs&, hipStream_t) { return hipSuccess; }
 hipError_t launch_precompute_f32(const PrecomputeArgs&, hipStream_t) { return hipSuccess; }
 hipError_t launch_append_bf16(const AppendArgs&, hipStream_t) { return hipSuccess; }
@@ -86,7 +86,66 @@ static int check(int batch, int Hq, int Hkv, const std::vector<int>& ks, const s
   return 0;
 }
 
+// bf16 prefill launches: several requests are sorted by descending keys per work item
+// (ceil(k_len / n_split)) and dealt over the XCDs (grid_per_xcd == 0); a single request
+// keeps the XCD-major mapping.  Either way the kernel's block -> item map covers every
+// work item exactly once, and every request appears exactly once.
+static int check_prefill_order(const std::vector<int>& ql, const std::vector<int>& kl) {
+  g_recs.clear();
+  const int batch = (int)ql.size(), Hq = 32, Hkv = 8;
+  std::vector<int> qs(batch), ks(batch), ag(batch, 0);
+  int64_t q_rows = 0, kv_rows = 0;
+  for (int b = 0; b < batch; ++b) { qs[b] = (int)q_rows; q_rows += ql[b]; ks[b] = (int)kv_rows; kv_rows += kl[b]; }
+  std::vector<int> ranks = {16};
+  std::vector<const void*> L = {(void*)0x100000}, B = {(void*)0x200000};
+  std::vector<int64_t> ldl = {16};
+  const size_t wsb = lra_attn_workspace_bytes(LRA_DTYPE_BF16, 0, batch, ql.data(), kl.data(), Hq, Hkv, 128, 16);
+  int rc = lra_attn_prefill(LRA_DTYPE_BF16, batch, Hq, Hkv, 128, qs.data(), ql.data(), ks.data(),
+                            kl.data(), ag.data(), (void*)0x1000, q_rows, (void*)0x2000, (void*)0x3000,
+                            kv_rows, 1, ranks.data(), L.data(), ldl.data(), B.data(), (void*)0x4000,
+                            wsb ? (void*)0x10000000 : nullptr, wsb, nullptr);
+  if (rc) { printf("rc %d: %s\n", rc, lra_last_error()); return 1; }
+  std::multiset<int> seen;
+  for (const Rec& r : g_recs) {
+    if (r.kind != 0) continue;
+    const lra::AttnArgs& a = r.a;
+    int64_t work = 0, prev = INT64_MAX;
+    for (int i = 0; i < a.n_req; ++i) {
+      const lra::ReqDesc& q = a.reqs[i];
+      seen.insert(q.q_start);
+      assert(q.work_start == work);
+      work += (int64_t)Hkv * q.n_rt * q.n_split;
+      const int64_t keys = (q.k_len + q.n_split - 1) / q.n_split;
+      if (a.n_req > 1) assert(keys <= prev);
+      prev = keys;
+    }
+    assert(work == a.n_work);
+    assert((a.n_req > 1) == (a.grid_per_xcd == 0));
+    std::vector<int> hit(a.n_work, 0);
+    for (int bid = 0; bid < r.grid; ++bid) {
+      const int w = a.grid_per_xcd > 0
+                        ? (bid & 7) * a.grid_per_xcd + (bid >> 3)
+                        : ((bid >> 3) / lra::kDealChunk) * (8 * lra::kDealChunk) +
+                              (bid & 7) * lra::kDealChunk + (bid >> 3) % lra::kDealChunk;
+      if (w < a.n_work) ++hit[w];
+    }
+    for (int w = 0; w < a.n_work; ++w) assert(hit[w] == 1);
+  }
+  for (int b = 0; b < batch; ++b) assert(seen.count(qs[b]) == 1);
+  return 0;
+}
+
 int main() {
+  // prefill: a mixed batch (one launch), 100 requests (two launches), one request
+  {
+    std::vector<int> ql, kl;
+    for (int i = 0; i < 32; ++i) { ql.push_back(1 + (i * 97) % 512); kl.push_back(ql.back() + 2048 + (i * 4441) % 14336); }
+    assert(!check_prefill_order(ql, kl));
+    ql.clear(); kl.clear();
+    for (int i = 0; i < 100; ++i) { ql.push_back(1 + (i * 37) % 300); kl.push_back(ql.back() + (i * 911) % 5000); }
+    assert(!check_prefill_order(ql, kl));
+    assert(!check_prefill_order({1024}, {9216}));
+  }
   // 16 contexts x 4 agents, G = 4: units of 4
   {
     std::vector<int> ks, kl, ag;
