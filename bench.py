@@ -117,14 +117,14 @@ def time_calls(fn, steps, warmup, flush=None):
 # what the same counter reads for a plain 1 GiB device copy); the per-kernel summaries and
 # the commands are under profiles/.  The figures describe the kernels built from sources
 # with this digest and are reported as null for any other sources.
-TRAFFIC_SOURCES_SHA256 = "56b731000996b9a6d11eed7afa1036f315693489984708529fc77794fce94758"
+TRAFFIC_SOURCES_SHA256 = "3e1f3cc1aa2808621a608b6eef0cce03cab4a48645505964ad0735018f3d20af"
 TRAFFIC_BYTES = {
-    "llama8b-prefill-1024q-9216k-r16": 127035600,
-    "decode-64x16384-r16": 4417532265,
-    "decode-shared-16x4x16384-r16": 1163159262,
-    "lr-precompute-32768x4096-3x64": 293967574,
-    "lr-append-64x4096-4x16": 6361086,
-    "longctx-prefill-512q-32768k-r64": 245418079,
+    "llama8b-prefill-1024q-9216k-r16": 126502389,
+    "decode-64x16384-r16": 4418132365,
+    "decode-shared-16x4x16384-r16": 1161602798,
+    "lr-precompute-32768x4096-3x64": 293967913,
+    "lr-append-64x4096-4x16": 6361059,
+    "longctx-prefill-512q-32768k-r64": 244895658,
 }
 
 
