@@ -87,6 +87,19 @@ def test_bf16_ragged_batch(shape):
     _cmp_full(prob, cpu, O)
 
 
+def test_bf16_many_requests_longest_first():
+    """150 prefill requests: three launches (64 requests each at most), each sorted longest
+    first and dealt over the XCDs; every request's rows must match the oracle."""
+    rng = np.random.default_rng(660)
+    k_len = [int(x) for x in rng.integers(1, 600, 150)]
+    q_len = [int(rng.integers(0, min(k, 40) + 1)) for k in k_len]
+    agents = [int(a) for a in rng.integers(0, 3, 150)]
+    prob = workloads.custom("bf16-many", "bf16", 16, 4, 128, (16, 0, 64), q_len, k_len, agents,
+                            seed=661)
+    cpu, dev = H.device_inputs(prob)
+    _cmp_full(prob, cpu, H.run_prefill(prob, dev))
+
+
 def test_bf16_lr_isolated_and_peaked():
     # V_base = 0 leaves only (P·L)·B, which the default tolerances would barely see.
     prob = workloads.custom("bf16-lr-only", "bf16", 8, 2, 128, (16, 64), [50, 120], [400, 900],
