@@ -117,7 +117,7 @@ def time_calls(fn, steps, warmup, flush=None):
 # what the same counter reads for a plain 1 GiB device copy); the per-kernel summaries and
 # the commands are under profiles/.  The figures describe the kernels built from sources
 # with this digest and are reported as null for any other sources.
-TRAFFIC_SOURCES_SHA256 = "3e1f3cc1aa2808621a608b6eef0cce03cab4a48645505964ad0735018f3d20af"
+TRAFFIC_SOURCES_SHA256 = "36666df55a655e1c4921db11f13458257cae723b215e525dea82d099b9cfadf1"
 TRAFFIC_BYTES = {
     "llama8b-prefill-1024q-9216k-r16": 126502389,
     "decode-64x16384-r16": 4418132365,

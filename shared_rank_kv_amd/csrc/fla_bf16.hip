@@ -74,10 +74,6 @@ __device__ __forceinline__ void wait_loads_but() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | N);
 }
 
-__device__ __forceinline__ float lane_bcast(float x, int src) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), src));
-}
-
 // LDS layouts of the 64-key tiles (rows are D*2 bytes; 16-byte chunk c of row k lives at
 // position c ^ swz(k)).  K is read by 32 consecutive rows at one chunk (ds_read_b128), V by
 // ds_read_b64_tr_b16 over 4 consecutive rows x 4 consecutive chunks per half-wave; each
