@@ -323,6 +323,9 @@ MUTATIONS = {
 }
 
 
+# a planted strict mask leaves a query row with no visible key: its softmax is 0/0 (NaN),
+# which the pins then reject, as they should
+@pytest.mark.filterwarnings("ignore:invalid value encountered:RuntimeWarning")
 @pytest.mark.parametrize("name", list(MUTATIONS))
 def test_planted_mistake_is_caught(name, monkeypatch):
     attr, fn = MUTATIONS[name]
