@@ -412,7 +412,8 @@ def environment():
     import subprocess
     import torch
     props = torch.cuda.get_device_properties(0)
-    env = {"device": props.name, "compute_units": props.multi_processor_count,
+    env = {"device": props.name, "arch": getattr(props, "gcnArchName", None),
+           "compute_units": props.multi_processor_count,
            "torch": torch.__version__, "hip": torch.version.hip}
     try:
         # rocm-smi is a Python script: run it with this interpreter, so no launcher (env)
