@@ -2,6 +2,8 @@
 algorithmic-work accounting used for the rooflines, and the planner's workspace sizing
 as reported through the C ABI (host code only; no kernel is launched)."""
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -228,3 +230,31 @@ def test_workspace_rejects_invalid_arguments(lra):
         lra.lra_attn_workspace_bytes(torch.bfloat16, False, [10], [50], 32, 8, 96, 16)
     with pytest.raises(lra.LraError):
         lra.lra_attn_workspace_bytes(torch.bfloat16, True, None, [0], 32, 8, 128, 16)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: --gpus above 1 exits with status 2 and says why, before
+    touching the GPU."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_bench_traffic_figures_follow_the_sources():
+    """The HBM traffic figures are reported only for the library sources they were
+    measured with (the digest covers the header and every source of liblra.so)."""
+    import importlib.util
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    spec = importlib.util.spec_from_file_location("bench_mod", os.path.join(root, "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    assert len(bench.TRAFFIC_SOURCES_SHA256) == 64
+    if bench.sources_sha256() == bench.TRAFFIC_SOURCES_SHA256:
+        assert bench.traffic_bytes("llama8b-prefill-1024q-9216k-r16") > 0
+    r = bench.roof(500.0, 2500.0, "TFLOP/s", "mfma", None)
+    assert r == {"bound": "mfma", "achieved": 500.0, "peak": 2500.0, "unit": "TFLOP/s",
+                 "frac": 0.2, "traffic": None}
