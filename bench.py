@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the Flash-LoRA-Attention hot path on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--mixed] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-mixed] [--no-cpu-baseline]
 
 Headline (the JSON line's `value`): bf16 Flash-LoRA-Attention prefill throughput in
 TFLOP/s (algorithmic FLOP) on the Llama-3-8B-shaped single-layer workload: 1024 new causal
@@ -18,7 +18,7 @@ flushed between calls of the HBM-bound ones):
   append      decode-step LR append: 64 new tokens x 4096 into 4 rank-16 caches (HBM GB/s)
   precompute  L = X·[A_1..A_3], X [32768, 4096], ranks 3 x 64              (HBM GB/s)
   longctx     512 queries over 32768 keys, rank 64, L from the precompute   (TFLOP/s)
-  mixed       (--mixed) 32 layers of a 32-request batch, ranks 8/16/32/64   (roofline time)
+  mixed       32 layers of a 32-request batch, ranks 8/16/32/64 (--no-mixed skips it)
 and the CPU fp64 oracle timed on a bounded sample of the headline workload.
 
 Prints ONE JSON line on stdout.  Inputs are seeded synthetic tensors resident in HBM
@@ -455,7 +455,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--mixed", action="store_true", help="also time the 32-layer mixed batch")
+    ap.add_argument("--mixed", action="store_true",
+                    help="time the 32-layer mixed batch (the default; kept for old command lines)")
+    ap.add_argument("--no-mixed", action="store_true", help="skip the 32-layer mixed batch")
     ap.add_argument("--only", choices=["prefill", "decode", "decode_shared", "append", "longctx",
                                        "mixed", "copy"],
                     help="time one workload only (for profiling); prints its JSON object. "
@@ -510,7 +512,7 @@ def main():
         out["precompute"], out["longctx_prefill"] = bench_longctx(args.steps, args.warmup, flush)
         del flush
         torch.cuda.empty_cache()
-        if args.mixed:
+        if not args.no_mixed:
             log("[bench] mixed 32-layer batch")
             out["mixed"] = bench_mixed(args.steps, args.warmup)
         log("[bench] ceilings")
