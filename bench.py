@@ -11,6 +11,8 @@ back to back between device synchronisations.
 
 Also reported, each timed on its own (HIP events around every call, the 256 MB MALL
 flushed between calls of the HBM-bound ones):
+  tiny_fp32   16 queries over 256 keys, 4 heads, head_dim 64, 2 agents of rank 8, fp32
+              (latency only)
   decode      64 requests x 16384 keys, one query each, rank 16, 4 agents  (HBM GB/s)
   decode_shared  16 contexts x 16384 keys, each read by all 4 agents (rank 16):
               64 requests whose K/V tiles are streamed once per context (HBM GB/s,
@@ -195,6 +197,20 @@ def bench_llama_prefill(steps, warmup):
     per, total = time_calls(fn, steps, warmup)
     flop, nbytes = accounting.attention_work(prob)
     return prob, cpu, dev, {"flop": flop, "bytes": nbytes, "per_ms": per, "total_ms": total}
+
+
+def bench_tiny_fp32(steps, warmup):
+    """The tiny fp32 workload (both agents in one call): launch- and latency-bound, so the
+    time is reported with neither roofline."""
+    from shared_rank_kv_amd import accounting, workloads
+    prob = workloads.tiny_fp32()
+    _, dev = upload(prob)
+    fn = prefill_call(prob, dev, workspace_for(prob, False))
+    per, _ = time_calls(fn, max(steps, 100), warmup)
+    flop, nbytes = accounting.attention_work(prob)
+    us = float(np.median(per)) * 1e3
+    return {"workload": prob.name, "dtype": "f32", "us_per_call": round(us, 2), "flop": flop,
+            "bytes": nbytes, "bound": "latency (launch of one small kernel)"}
 
 
 def bench_decode(steps, warmup, flush):
@@ -501,6 +517,8 @@ def main():
         log("[bench] cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline(prob, cpu)
     if not args.only:
+        log("[bench] tiny fp32")
+        out["tiny_fp32"] = bench_tiny_fp32(args.steps, args.warmup)
         flush = Flusher()
         log("[bench] decode")
         out["decode"] = bench_decode(args.steps, args.warmup, flush)

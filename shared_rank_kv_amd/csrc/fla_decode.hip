@@ -469,26 +469,31 @@ __global__ __launch_bounds__(256, RB == 2 ? 1 : 2) void fla_decode_shared_bf16(c
   LDS char* lt = vt + VT;
 
   // LR rows of every member slot through a buffer resource that covers exactly the
-  // request's rows: reads past them, past the row's rank (the row continues into padding
-  // or the next row; those columns are never used), or of an empty slot return zeros
-  // or unused values and never leave the member's cache.  Each load unit u = lane + 64 i
-  // covers row u / LCH, 16-byte chunk u % LCH of the 32 x (32 RB) tile.
+  // request's rows: reads past them, or of an empty slot, return zeros and never leave the
+  // member's cache.  Chunks at or past a member's own rank are addressed out of range, so
+  // they read zeros too: the row's padding (or the next row) never enters the shared LR
+  // accumulator, where a non-finite value times another member's masked P (0·NaN) would
+  // reach that member's columns.  Each load unit u = lane + 64 i covers row u / LCH,
+  // 16-byte chunk u % LCH of the 32 x (32 RB) tile.
   __amdgpu_buffer_rsrc_t lrs[NM];
-  int ldl_b[NM];
+  int ldl_b[NM], rank_m[NM];
 #pragma unroll
   for (int m = 0; m < NM; ++m) {
     int bytes = 0;
     const void* base = A->K;
     ldl_b[m] = 0;
+    rank_m[m] = 0;
     if (RB && m < nm) {
       const AgentDesc& AG = A->agents[A->reqs[b + m].agent];
       if (AG.rank > 0) {
         base = (const bf16*)AG.L + (int64_t)k_start * AG.ldl;
         bytes = (int)((int64_t)Lk * AG.ldl * 2);
         ldl_b[m] = (int)(AG.ldl * 2);
+        rank_m[m] = AG.rank;
       }
     }
     ldl_b[m] = __builtin_amdgcn_readfirstlane(ldl_b[m]);
+    rank_m[m] = __builtin_amdgcn_readfirstlane(rank_m[m]);
     lrs[m] = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0,
                                                __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
   }
@@ -531,10 +536,10 @@ __global__ __launch_bounds__(256, RB == 2 ? 1 : 2) void fla_decode_shared_bf16(c
 #pragma unroll
       for (int i = 0; i < NL; ++i) {
         const int key = min(k0 + l_row[i], ke - 1);
-        const int u = lane + 64 * i;
+        const int c = (lane + 64 * i) % LCH;
+        const int off = c * 8 < rank_m[m] ? key * ldl_b[m] + c * 16 : 0x7ffffff0;
         lreg[m][i] = __builtin_bit_cast(
-            u32x4, __builtin_amdgcn_raw_buffer_load_b128(lrs[m], key * ldl_b[m] + (u % LCH) * 16,
-                                                         0, 0));
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(lrs[m], off, 0, 0));
       }
   };
   auto store_v = [&]() {
@@ -728,7 +733,7 @@ __global__ __launch_bounds__(256, RB == 2 ? 1 : 2) void fla_decode_shared_bf16(c
         o1 += wgt[wv] * v[1];
       }
       if (RB) {
-        // columns of P·L_a past the member's rank hold unrelated products: skipped
+        // columns of P·L_a at or past the member's rank are zero: skipped
 #pragma unroll
         for (int k = 0; k < RMAX; ++k) {
           if (k < brank) {

@@ -9,6 +9,7 @@ missing (build it with ``python -m shared_rank_kv_amd.build``).
 
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -88,10 +89,8 @@ def _dtype(t):
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
-def _stream(stream):
-    if stream is None:
-        stream = torch.cuda.current_stream()
-    return ctypes.c_void_p(stream.cuda_stream)
+def _nullctx():
+    return contextlib.nullcontext()
 
 
 def _check(rc):
@@ -103,6 +102,60 @@ def _dev(t, name):
     if not (t.is_cuda and t.is_contiguous()):
         raise ValueError(f"{name} must be a contiguous GPU tensor")
     return t
+
+
+def _like(t, ref, name):
+    if t.dtype != ref.dtype or t.device != ref.device:
+        raise ValueError(f"{name} must be a {ref.dtype} tensor on {ref.device} "
+                         f"(got {t.dtype} on {t.device})")
+
+
+def _adapter_ranks(Q, L, B, kv_rows, Hkv, D):
+    """Checks every agent's LR cache and up-projection against the call (the C ABI cannot
+    see dtypes, devices or a transposed view) and returns the ranks.  L[a] is None (rank 0)
+    or a [kv_rows, r_a] tensor with unit column stride (its row stride may exceed r_a);
+    B[a] is a contiguous [r_a, Hkv*D] tensor."""
+    if len(L) != len(B):
+        raise ValueError(f"{len(L)} LR caches but {len(B)} up-projections")
+    ranks = []
+    for a, (l, b) in enumerate(zip(L, B)):
+        if l is None or l.shape[-1] == 0:
+            ranks.append(0)
+            continue
+        _like(l, Q, f"L[{a}]")
+        if l.dim() != 2 or l.stride(1) != 1 or l.shape[0] < kv_rows:
+            raise ValueError(f"L[{a}] must be [kv_rows >= {kv_rows}, r] with unit column "
+                             f"stride (got shape {tuple(l.shape)}, strides {l.stride()})")
+        r = int(l.shape[1])
+        if b is None:
+            raise ValueError(f"B[{a}] is None for an agent of rank {r}")
+        _like(b, Q, f"B[{a}]")
+        if tuple(b.shape) != (r, Hkv * D) or not b.is_contiguous():
+            raise ValueError(f"B[{a}] must be a contiguous [{r}, {Hkv * D}] tensor "
+                             f"(got shape {tuple(b.shape)}, strides {b.stride()})")
+        ranks.append(r)
+    return ranks
+
+
+def _lr_outputs(X, A_cat, ranks, L_out):
+    """Checks of the precompute / append operands the C ABI cannot see."""
+    if X.dim() != 2 or A_cat.dim() != 2 or X.stride(1) != 1 or A_cat.stride(1) != 1:
+        raise ValueError("X and A_cat must be 2-D with unit column stride")
+    _like(A_cat, X, "A_cat")
+    if A_cat.shape[0] != X.shape[1] or A_cat.shape[1] < sum(int(r) for r in ranks):
+        raise ValueError(f"A_cat {tuple(A_cat.shape)} does not match d_model {X.shape[1]} "
+                         f"and ranks {tuple(ranks)}")
+    if len(L_out) != len(ranks):
+        raise ValueError(f"{len(L_out)} outputs for {len(ranks)} ranks")
+    for a, (t, r) in enumerate(zip(L_out, ranks)):
+        if int(r) == 0 and t is None:
+            continue
+        _like(t, X, f"L_out[{a}]")
+        if t.dim() != 2 or t.stride(1) != 1 or t.shape[1] != int(r):
+            raise ValueError(f"L_out[{a}] must be [rows, {r}] with unit column stride "
+                             f"(got shape {tuple(t.shape)}, strides {t.stride()})")
+    if not X.is_cuda:
+        raise ValueError("X must be a GPU tensor")
 
 
 # ---------------------------------------------------------------------------------------
@@ -137,15 +190,25 @@ def _workspace(nbytes, device, workspace):
 
 class Prepared:
     """A marshalled call: the ctypes arguments (and the host arrays and tensors they point
-    to) are built once; calling it only runs the C entry point on the current stream."""
+    to) are built once; calling it only runs the C entry point on the given stream (default:
+    the current one).
 
-    def __init__(self, cfn, args, keep, result, stream_index):
+    Tensors the binding allocated itself (`owned`: a workspace, an output) are recorded on
+    the stream each call runs on, so torch's caching allocator does not hand their memory
+    to another stream's allocation while that call's kernels may still use it, even once
+    this object is gone."""
+
+    def __init__(self, cfn, args, keep, result, stream_index, owned=()):
         self._cfn, self._args, self._keep, self.result = cfn, list(args), keep, result
         self._si = stream_index
+        self._owned = tuple(t for t in owned if t is not None)
 
     def __call__(self, stream=None):
-        self._args[self._si] = _stream(stream)
+        s = torch.cuda.current_stream() if stream is None else stream
+        self._args[self._si] = ctypes.c_void_p(s.cuda_stream)
         _check(self._cfn(*self._args))
+        for t in self._owned:
+            t.record_stream(s)
         return self.result
 
 
@@ -156,10 +219,10 @@ def prepare_precompute_lr(X, A_cat, ranks, L_out):
     L_out: list of [T, r_a] GPU tensors (row stride = stride(0)).
     """
     _dtype(X)
-    assert X.dim() == 2 and A_cat.dim() == 2 and X.stride(1) == 1 and A_cat.stride(1) == 1
+    _lr_outputs(X, A_cat, ranks, L_out)
     rk, rkp = _i32(ranks)
     pk, ptrs = _ptrs(L_out)
-    ld, ldp = _i64([t.stride(0) for t in L_out])
+    ld, ldp = _i64([t.stride(0) if t is not None else 0 for t in L_out])
     args = (_dtype(X), X.shape[0], X.shape[1], X.data_ptr(), X.stride(0), A_cat.data_ptr(),
             A_cat.stride(0), len(rk), rkp, ptrs, ldp, None)
     return Prepared(lib.lra_precompute_lr, args, (X, A_cat, L_out, rk, pk, ld), L_out, 11)
@@ -178,7 +241,7 @@ def prepare_append_lr(X, A_cat, ranks, L_out, rows):
     distinct cache rows.
     """
     _dtype(X)
-    assert X.dim() == 2 and A_cat.dim() == 2 and X.stride(1) == 1 and A_cat.stride(1) == 1
+    _lr_outputs(X, A_cat, ranks, L_out)
     rk, rkp = _i32(ranks)
     pk, ptrs = _ptrs(L_out)
     ld, ldp = _i64([t.stride(0) if t is not None else 0 for t in L_out])
@@ -198,10 +261,12 @@ def prepare_attn_prefill(Q, K_base, V_base, L, B, q_start, q_len, k_start, k_len
                          O=None, workspace=None):
     """Prepared lra_attn_prefill (see lra_attn_prefill)."""
     _dev(Q, "Q"), _dev(K_base, "K_base"), _dev(V_base, "V_base")
+    _like(K_base, Q, "K_base"), _like(V_base, Q, "V_base")
     dt = _dtype(Q)
     q_rows, Hq, D = Q.shape
     kv_rows, Hkv, _ = K_base.shape
-    ranks = [0 if (l is None) else l.shape[1] for l in L]
+    ranks = _adapter_ranks(Q, L, B, kv_rows, Hkv, D)
+    owned_O = O is None
     if O is None:
         O = torch.empty_like(Q)
     qs, qsp = _i32(q_start)
@@ -221,7 +286,8 @@ def prepare_attn_prefill(Q, K_base, V_base, L, B, q_start, q_len, k_start, k_len
             K_base.data_ptr(), V_base.data_ptr(), kv_rows, len(rk), rkp, lp, ldp, bp,
             O.data_ptr(), ws.data_ptr() if ws is not None else None, ws_bytes, None)
     keep = (Q, K_base, V_base, L, B, O, ws, qs, ql, ks, kl, ag, rk, lk, ld, bk)
-    return Prepared(lib.lra_attn_prefill, args, keep, O, 23)
+    owned = (O if owned_O else None, ws if workspace is None else None)
+    return Prepared(lib.lra_attn_prefill, args, keep, O, 23, owned)
 
 
 def lra_attn_prefill(Q, K_base, V_base, L, B, q_start, q_len, k_start, k_len, agent_idx, O=None,
@@ -231,18 +297,21 @@ def lra_attn_prefill(Q, K_base, V_base, L, B, q_start, q_len, k_start, k_len, ag
     Q [q_rows, Hq, D]; K_base, V_base [kv_rows, Hkv, D]; L: list of per-agent [kv_rows, r_a]
     LR caches (row stride may exceed r_a; None for rank 0); B: list of [r_a, Hkv*D].
     """
-    return prepare_attn_prefill(Q, K_base, V_base, L, B, q_start, q_len, k_start, k_len,
-                                agent_idx, O, workspace)(stream)
+    with torch.cuda.stream(stream) if stream is not None else _nullctx():
+        return prepare_attn_prefill(Q, K_base, V_base, L, B, q_start, q_len, k_start, k_len,
+                                    agent_idx, O, workspace)(stream)
 
 
 def prepare_attn_decode(Q, K_base, V_base, L, B, k_start, k_len, agent_idx, O=None,
                         workspace=None):
     """Prepared lra_attn_decode (see lra_attn_decode)."""
     _dev(Q, "Q"), _dev(K_base, "K_base"), _dev(V_base, "V_base")
+    _like(K_base, Q, "K_base"), _like(V_base, Q, "V_base")
     dt = _dtype(Q)
     batch, Hq, D = Q.shape
     kv_rows, Hkv, _ = K_base.shape
-    ranks = [0 if (l is None) else l.shape[1] for l in L]
+    ranks = _adapter_ranks(Q, L, B, kv_rows, Hkv, D)
+    owned_O = O is None
     if O is None:
         O = torch.empty_like(Q)
     ks, ksp = _i32(k_start)
@@ -260,12 +329,14 @@ def prepare_attn_decode(Q, K_base, V_base, L, B, k_start, k_len, agent_idx, O=No
             V_base.data_ptr(), kv_rows, len(rk), rkp, lp, ldp, bp, O.data_ptr(),
             ws.data_ptr() if ws is not None else None, ws_bytes, None)
     keep = (Q, K_base, V_base, L, B, O, ws, ks, kl, ag, rk, lk, ld, bk)
-    return Prepared(lib.lra_attn_decode, args, keep, O, 20)
+    owned = (O if owned_O else None, ws if workspace is None else None)
+    return Prepared(lib.lra_attn_decode, args, keep, O, 20, owned)
 
 
 def lra_attn_decode(Q, K_base, V_base, L, B, k_start, k_len, agent_idx, O=None, workspace=None,
                     stream=None):
     """One query token per request: Q, O [batch, Hq, D]; request b attends to key rows
     [k_start[b], k_start[b] + k_len[b]) of its agent."""
-    return prepare_attn_decode(Q, K_base, V_base, L, B, k_start, k_len, agent_idx, O,
-                               workspace)(stream)
+    with torch.cuda.stream(stream) if stream is not None else _nullctx():
+        return prepare_attn_decode(Q, K_base, V_base, L, B, k_start, k_len, agent_idx, O,
+                                   workspace)(stream)

@@ -135,7 +135,103 @@ static int check_prefill_order(const std::vector<int>& ql, const std::vector<int
   return 0;
 }
 
+// Validation paths of every entry point: each malformed or unsupported call returns its
+// status with a message and launches nothing; a valid call clears the message.
+static void expect(int rc, int want, const char* what) {
+  if (rc != want) { printf("%s: rc %d, want %d (%s)\n", what, rc, want, lra_last_error()); abort(); }
+  if (want != LRA_OK && lra_last_error()[0] == '\0') { printf("%s: no message\n", what); abort(); }
+  if (want == LRA_OK && lra_last_error()[0] != '\0') { printf("%s: stale message\n", what); abort(); }
+}
+
+struct PrefillCall {
+  int dtype = LRA_DTYPE_BF16, batch = 2, Hq = 8, Hkv = 2, D = 128;
+  std::vector<int> qs = {0, 10}, ql = {10, 5}, ks = {0, 0}, kl = {100, 50}, ag = {0, 1};
+  int64_t q_rows = 15, kv_rows = 100;
+  std::vector<int> ranks = {16, 8};
+  std::vector<const void*> L = {(void*)0x100000, (void*)0x101000};
+  std::vector<int64_t> ldl = {16, 8};
+  std::vector<const void*> B = {(void*)0x200000, (void*)0x202000};
+  size_t ws_bytes = (size_t)1 << 30;
+  int run() {
+    g_recs.clear();
+    const int rc = lra_attn_prefill(dtype, batch, Hq, Hkv, D, qs.data(), ql.data(), ks.data(),
+                                    kl.data(), ag.data(), (void*)0x1000, q_rows, (void*)0x2000,
+                                    (void*)0x3000, kv_rows, (int)ranks.size(), ranks.data(),
+                                    L.data(), ldl.data(), B.data(), (void*)0x4000,
+                                    (void*)0x10000000, ws_bytes, nullptr);
+    if (rc != LRA_OK) assert(g_recs.empty());
+    return rc;
+  }
+};
+
+static void check_validation() {
+  expect(PrefillCall().run(), LRA_OK, "valid prefill");
+  { PrefillCall c; c.dtype = 7; expect(c.run(), LRA_ERR_INVALID, "dtype"); }
+  { PrefillCall c; c.batch = -1; expect(c.run(), LRA_ERR_INVALID, "negative batch"); }
+  { PrefillCall c; c.batch = LRA_MAX_BATCH + 1; expect(c.run(), LRA_ERR_UNSUPPORTED, "batch cap"); }
+  { PrefillCall c; c.Hq = 6; c.Hkv = 4; expect(c.run(), LRA_ERR_INVALID, "Hq % Hkv"); }
+  { PrefillCall c; c.Hq = 32; c.Hkv = 2; expect(c.run(), LRA_ERR_UNSUPPORTED, "group > 8"); }
+  { PrefillCall c; c.D = 96; expect(c.run(), LRA_ERR_UNSUPPORTED, "head_dim"); }
+  { PrefillCall c; c.ql[1] = 60; expect(c.run(), LRA_ERR_INVALID, "q_len > k_len"); }
+  { PrefillCall c; c.qs[1] = 5; expect(c.run(), LRA_ERR_INVALID, "overlapping query rows"); }
+  { PrefillCall c; c.ks[0] = 1; expect(c.run(), LRA_ERR_INVALID, "key rows past kv_rows"); }
+  { PrefillCall c; c.ag[1] = 2; expect(c.run(), LRA_ERR_INVALID, "agent index"); }
+  { PrefillCall c; c.ranks[0] = 12; expect(c.run(), LRA_ERR_UNSUPPORTED, "rank % 8"); }
+  { PrefillCall c; c.ranks[0] = 72; c.ldl[0] = 72; expect(c.run(), LRA_ERR_UNSUPPORTED, "rank cap"); }
+  { PrefillCall c; c.ldl[0] = 8; expect(c.run(), LRA_ERR_INVALID, "ldl < rank"); }
+  { PrefillCall c; c.ldl[0] = 20; expect(c.run(), LRA_ERR_INVALID, "ldl % 8"); }
+  { PrefillCall c; c.L[1] = (void*)0x101004; expect(c.run(), LRA_ERR_INVALID, "L alignment"); }
+  { PrefillCall c; c.ws_bytes = 16; c.kl = {3000, 50}; c.kv_rows = 3000;
+    // few row tiles over many keys: the planner splits the keys, which needs a workspace
+    const size_t need = lra_attn_workspace_bytes(LRA_DTYPE_BF16, 0, 2, c.ql.data(), c.kl.data(), 8, 2, 128, 16);
+    assert(need > 16);
+    expect(c.run(), LRA_ERR_WORKSPACE, "workspace too small");
+    c.ws_bytes = need;
+    expect(c.run(), LRA_OK, "workspace of the queried size"); }
+  { PrefillCall c; c.ql = {0, 0}; expect(c.run(), LRA_OK, "empty requests"); assert(g_recs.empty()); }
+  assert(lra_attn_workspace_bytes(LRA_DTYPE_BF16, 0, 1, nullptr, nullptr, 8, 2, 128, 16) == (size_t)-1);
+  { const int ql = 5, kl = 4;
+    assert(lra_attn_workspace_bytes(LRA_DTYPE_BF16, 0, 1, &ql, &kl, 8, 2, 128, 16) == (size_t)-1); }
+  // decode
+  { const int ks[2] = {0, 0}, kl[2] = {10, 0}, ag[2] = {0, 0}, r = 16;
+    const void* L = (void*)0x100000; const void* B = (void*)0x200000; const int64_t ldl = 16;
+    expect(lra_attn_decode(LRA_DTYPE_BF16, 2, 8, 2, 128, ks, kl, ag, (void*)0x1000, (void*)0x2000,
+                           (void*)0x3000, 100, 1, &r, &L, &ldl, &B, (void*)0x4000, nullptr, 0, nullptr),
+           LRA_ERR_INVALID, "decode with an empty context"); }
+  // precompute and append
+  const int ranks[3] = {64, 64, 64};
+  void* outs[3] = {(void*)0x100000, (void*)0x200000, (void*)0x300000};
+  const int64_t ldl[3] = {64, 64, 64};
+  expect(lra_precompute_lr(LRA_DTYPE_BF16, 100, 4096, (void*)0x1000, 4096, (void*)0x2000, 192, 3,
+                           ranks, outs, ldl, nullptr), LRA_OK, "valid precompute");
+  expect(lra_precompute_lr(LRA_DTYPE_BF16, 100, 100, (void*)0x1000, 104, (void*)0x2000, 192, 3,
+                           ranks, outs, ldl, nullptr), LRA_ERR_UNSUPPORTED, "d_model % 8");
+  expect(lra_precompute_lr(LRA_DTYPE_BF16, 100, 4096, (void*)0x1000, 4000, (void*)0x2000, 192, 3,
+                           ranks, outs, ldl, nullptr), LRA_ERR_INVALID, "ldx < d_model");
+  expect(lra_precompute_lr(LRA_DTYPE_BF16, 100, 4096, (void*)0x1000, 4096, (void*)0x2000, 100, 3,
+                           ranks, outs, ldl, nullptr), LRA_ERR_INVALID, "lda < sum of ranks");
+  { const int big[5] = {64, 64, 64, 64, 64}; void* o5[5] = {outs[0], outs[1], outs[2], outs[0], outs[1]};
+    const int64_t l5[5] = {64, 64, 64, 64, 64};
+    expect(lra_precompute_lr(LRA_DTYPE_BF16, 100, 4096, (void*)0x1000, 4096, (void*)0x2000, 320, 5,
+                             big, o5, l5, nullptr), LRA_ERR_UNSUPPORTED, "sum of ranks > 256"); }
+  { const int rows[3] = {5, 9, 5};
+    expect(lra_append_lr(LRA_DTYPE_BF16, 3, 4096, (void*)0x1000, 4096, (void*)0x2000, 192, 3, ranks,
+                         outs, ldl, rows, 100, nullptr), LRA_ERR_INVALID, "duplicate append rows"); }
+  { const int rows[2] = {5, 100};
+    expect(lra_append_lr(LRA_DTYPE_BF16, 2, 4096, (void*)0x1000, 4096, (void*)0x2000, 192, 3, ranks,
+                         outs, ldl, rows, 100, nullptr), LRA_ERR_INVALID, "append row out of range"); }
+  { std::vector<int> rows(LRA_MAX_BATCH + 1);
+    for (size_t i = 0; i < rows.size(); ++i) rows[i] = (int)i;
+    expect(lra_append_lr(LRA_DTYPE_BF16, (int)rows.size(), 4096, (void*)0x1000, 4096, (void*)0x2000,
+                         192, 3, ranks, outs, ldl, rows.data(), 1 << 20, nullptr),
+           LRA_ERR_UNSUPPORTED, "append batch cap"); }
+  { const int rows[2] = {5, 9};
+    expect(lra_append_lr(LRA_DTYPE_BF16, 2, 4096, (void*)0x1000, 4096, (void*)0x2000, 192, 3, ranks,
+                         outs, ldl, rows, 100, nullptr), LRA_OK, "valid append"); }
+}
+
 int main() {
+  check_validation();
   // prefill: a mixed batch (one launch), 100 requests (two launches), one request
   {
     std::vector<int> ql, kl;

@@ -248,3 +248,56 @@ def test_decode_rejections():
     assert "q_len" in lra.lra_last_error()
     assert call([100, 101]) == lra.LRA_ERR_INVALID        # past kv_rows
     assert call([100, 100], agent=(0, 1)) == lra.LRA_ERR_INVALID
+
+
+# ---------------------------------------------------------------------------------------
+# Checks the Python binding makes before it marshals a call: the C ABI receives raw
+# pointers and strides, so a wrong dtype, device or a transposed view of an LR cache or
+# an up-projection would be misread there without an error.
+# ---------------------------------------------------------------------------------------
+
+def test_binding_checks_adapter_tensors():
+    import torch
+    bf = torch.bfloat16
+    Q = torch.zeros(4, 8, 128, dtype=bf)
+    L = torch.zeros(100, 16, dtype=bf)
+    B = torch.zeros(16, 2 * 128, dtype=bf)
+    assert lra._adapter_ranks(Q, [L, None], [B, None], 100, 2, 128) == [16, 0]
+    # a column view of a wider buffer (row stride 64) is a valid LR cache
+    assert lra._adapter_ranks(Q, [torch.zeros(100, 64, dtype=bf)[:, :16]], [B], 100, 2, 128) == [16]
+    bad = [
+        ([L.float()], [B], "L[0] must be a torch.bfloat16"),
+        ([L], [B.float()], "B[0] must be a torch.bfloat16"),
+        ([torch.zeros(16, 100, dtype=bf).t()], [B], "unit column stride"),
+        ([L[:50]], [B], "kv_rows >= 100"),
+        ([L], [torch.zeros(256, 16, dtype=bf).t()], "contiguous [16, 256]"),
+        ([L], [torch.zeros(16, 128, dtype=bf)], "contiguous [16, 256]"),
+        ([L], [None], "B[0] is None"),
+        ([L, L], [B], "2 LR caches but 1"),
+    ]
+    for Ls, Bs, frag in bad:
+        with pytest.raises(ValueError) as e:
+            lra._adapter_ranks(Q, Ls, Bs, 100, 2, 128)
+        assert frag in str(e.value), (frag, str(e.value))
+
+
+def test_binding_checks_precompute_operands():
+    import torch
+    bf = torch.bfloat16
+    X = torch.zeros(10, 64, dtype=bf)
+    A = torch.zeros(64, 24, dtype=bf)
+    outs = [torch.zeros(10, 8, dtype=bf), torch.zeros(10, 16, dtype=bf)]
+    bad = [
+        (X, A.float(), outs, "A_cat must be a torch.bfloat16"),
+        (X, A.t(), outs, "unit column stride"),
+        (X, A[:32], outs, "does not match d_model"),
+        (X, A[:, :16], outs, "does not match d_model"),
+        (X, A, outs[:1], "1 outputs for 2 ranks"),
+        (X, A, [outs[0].float(), outs[1]], "L_out[0] must be a torch.bfloat16"),
+        (X, A, [outs[0], torch.zeros(16, 10, dtype=bf).t()], "L_out[1] must be [rows, 16]"),
+        (X, A, outs, "X must be a GPU tensor"),     # every other check passes on the CPU
+    ]
+    for x, a, o, frag in bad:
+        with pytest.raises(ValueError) as e:
+            lra._lr_outputs(x, a, (8, 16), o)
+        assert frag in str(e.value), (frag, str(e.value))

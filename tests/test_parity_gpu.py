@@ -234,6 +234,41 @@ def test_bf16_decode_shared_lr_cache():
     _cmp_full(prob, cpu, H.run_decode(prob, dev), what="shared LR cache")
 
 
+def test_bf16_lr_cache_padding_never_read():
+    """LR caches that are column views of wider buffers whose padding holds NaN: a unit of
+    the shared-context decode mixes ranks 8 and 64 (one accumulator serves both members),
+    and prefill and ungrouped decode read the same views.  No padding value may reach an
+    output."""
+    prob = workloads.shared_decode("bf16-padding", 32, 8, 128, (8, 64, 16),
+                                   [(1500, [0, 1, 2, 0]), (300, [1, 0])], seed=695)
+    cpu, dev = H.device_inputs(prob)
+    views = []
+    for a, L in enumerate(dev["L"]):
+        buf = torch.full((prob.kv_rows, 64 + 8), float("nan"), dtype=torch.bfloat16, device="cuda")
+        buf[:, :L.shape[1]] = L
+        views.append(buf[:, :L.shape[1]])
+    dev["L"] = views
+    grouped = H.run_decode(prob, dev)
+    assert torch.isfinite(grouped.float()).all()
+    _cmp_full(prob, cpu, grouped, what="shared decode, NaN padding")
+    os.environ["LRA_DECODE_GROUP"] = "0"
+    try:
+        single = H.run_decode(prob, dev)
+    finally:
+        del os.environ["LRA_DECODE_GROUP"]
+    _cmp_full(prob, cpu, single, what="decode, NaN padding")
+    pre = workloads.custom("bf16-padding-prefill", "bf16", 32, 8, 128, (8, 64, 16), [40, 7, 90],
+                           [1500, 300, 1500], [0, 1, 2], seed=696)
+    cpu, dev = H.device_inputs(pre)
+    views = []
+    for L in dev["L"]:
+        buf = torch.full((pre.kv_rows, 72), float("nan"), dtype=torch.bfloat16, device="cuda")
+        buf[:, :L.shape[1]] = L
+        views.append(buf[:, :L.shape[1]])
+    dev["L"] = views
+    _cmp_full(pre, cpu, H.run_prefill(pre, dev), what="prefill, NaN padding")
+
+
 # ---------------------------------------------------------------------------------------
 # LR precompute
 # ---------------------------------------------------------------------------------------

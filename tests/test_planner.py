@@ -29,3 +29,4 @@ def test_planner_units_and_launches(tmp_path):
     r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "planner checks passed" in r.stdout
+

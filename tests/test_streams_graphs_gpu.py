@@ -73,6 +73,42 @@ def test_calls_on_a_side_stream(lra, monkeypatch):
     assert torch.equal(O_p, want_p) and torch.equal(O_d, want_d)
 
 
+def test_one_shot_call_on_a_side_stream_keeps_its_scratch(lra, monkeypatch):
+    """A one-shot call with stream=side and no workspace: the binding allocates the
+    workspace and the output itself, queues the split kernels and the combine pass on the
+    side stream and returns.  Memory allocated and filled on the default stream right after
+    must not land in that scratch while the side stream may still use it."""
+    monkeypatch.setenv("LRA_PREFILL_TARGET_WG", "64")
+    pre, dec = _problems()
+    cpu_p, dev_p = H.device_inputs(pre)
+    cpu_d, dev_d = H.device_inputs(dec)
+    want_p = H.run_prefill(pre, dev_p).clone()
+    want_d = H.run_decode(dec, dev_d).clone()
+    ws_p = lra.lra_attn_workspace_bytes(torch.bfloat16, False, pre.q_len, pre.k_len, 8, 2, 128, 32)
+    ws_d = lra.lra_attn_workspace_bytes(torch.bfloat16, True, None, dec.k_len, 32, 8, 128, 64)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for _ in range(3):
+        outs.append(lra.lra_attn_prefill(dev_p["Q"], dev_p["K"], dev_p["V"], dev_p["L"],
+                                         dev_p["B"], pre.q_start, pre.q_len, pre.k_start,
+                                         pre.k_len, pre.agent_idx, stream=side))
+        outs.append(lra.lra_attn_decode(dev_d["Q"], dev_d["K"], dev_d["V"], dev_d["L"],
+                                        dev_d["B"], dec.k_start, dec.k_len, dec.agent_idx,
+                                        stream=side))
+        # blocks of the scratch's own sizes, written on the default stream at once
+        junk = [torch.full((n,), 0x7F, dtype=torch.uint8, device="cuda")
+                for n in (ws_p, ws_d, ws_p, ws_d) if n]
+        junk += [torch.full_like(dev_p["Q"], 9.0), torch.full_like(dev_d["Q"], 9.0)]
+        del junk
+    side.synchronize()
+    torch.cuda.synchronize()
+    for i, O in enumerate(outs):
+        assert torch.equal(O, want_p if i % 2 == 0 else want_d), f"call {i}"
+    H.assert_bf16_close(want_p.float().cpu().numpy(), H.oracle_all(pre, cpu_p), "prefill")
+    H.assert_bf16_close(want_d.float().cpu().numpy(), H.oracle_all(dec, cpu_d), "decode")
+
+
 def test_graph_capture_and_replay(lra, monkeypatch):
     monkeypatch.setenv("LRA_PREFILL_TARGET_WG", "64")
     pre, dec = _problems()
