@@ -178,6 +178,31 @@ int lra_attn_decode(int dtype, int32_t batch,
                     void* stream);
 
 /*
+ * lra_attn_decode_noalloc -- lra_attn_decode for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same arguments and results without `workspace`.  The split-key scratch is a fixed
+ * array of LRA_NOALLOC_SCRATCH_BYTES bytes inside this library, one copy per GPU, held
+ * until the process ends; the call allocates nothing.  A call whose plan needs more scratch
+ * (lra_attn_workspace_bytes(dtype, 1, ...) above the limit) returns LRA_ERR_WORKSPACE and
+ * queues nothing.  The scratch needs no initial contents.  Every call on one GPU uses that
+ * GPU's single array, so two calls whose work may overlap in time on one GPU (other
+ * streams, or other host threads) race on it and must be ordered by the caller; calls
+ * queued on one stream are ordered already.
+ */
+#define LRA_NOALLOC_SCRATCH_BYTES (32u << 20)
+int lra_attn_decode_noalloc(int dtype, int32_t batch,
+                            int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                            const int32_t* k_start, const int32_t* k_len,
+                            const int32_t* agent_idx,
+                            const void* Q,
+                            const void* K_base, const void* V_base, int64_t kv_rows,
+                            int32_t n_agents, const int32_t* ranks,
+                            const void* const* L, const int64_t* ldl,
+                            const void* const* B,
+                            void* O,
+                            void* stream);
+
+/*
  * lra_attn_workspace_bytes -- scratch bytes the call with these arguments needs
  * (is_decode = 0: lra_attn_prefill, 1: lra_attn_decode; q_len is ignored for decode and
  * may be NULL).  max_rank is the largest r_a of the call.  Returns 0 when no scratch is

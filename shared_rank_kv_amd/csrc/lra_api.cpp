@@ -486,6 +486,10 @@ int check_lr_args(int dtype, int64_t T, int64_t d_model, const void* X, int64_t 
 
 }  // namespace
 
+namespace lra {
+int report_error(int code, const char* msg) { return fail(code, "%s", msg); }
+}  // namespace lra
+
 extern "C" {
 
 const char* lra_last_error(void) { return g_err; }

@@ -97,6 +97,9 @@ struct AppendArgs {
   int32_t rows[kAppendRows];
 };
 
+// Sets the calling thread's lra_last_error() message and returns `code`.
+int report_error(int code, const char* msg);
+
 // Launchers (return the HIP status of the launch).
 hipError_t launch_prefill_bf16(const AttnArgs& a, int head_dim, int max_rank, int n_grid,
                                hipStream_t s);

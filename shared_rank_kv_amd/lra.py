@@ -20,8 +20,9 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblra.so")
 
 LRA_OK, LRA_ERR_INVALID, LRA_ERR_UNSUPPORTED, LRA_ERR_WORKSPACE, LRA_ERR_HIP = range(5)
 LRA_DTYPE_F32, LRA_DTYPE_BF16 = 0, 1
+NOALLOC_SCRATCH_BYTES = 32 << 20      # LRA_NOALLOC_SCRATCH_BYTES of include/lra.h
 SYMBOLS = ("lra_precompute_lr", "lra_append_lr", "lra_attn_prefill", "lra_attn_decode",
-           "lra_attn_workspace_bytes", "lra_last_error")
+           "lra_attn_decode_noalloc", "lra_attn_workspace_bytes", "lra_last_error")
 
 _c_i32p = ctypes.POINTER(ctypes.c_int32)
 _c_i64p = ctypes.POINTER(ctypes.c_int64)
@@ -51,6 +52,10 @@ def _load():
     lib.lra_attn_decode.argtypes = [ctypes.c_int, I, I, I, I, _c_i32p, _c_i32p, _c_i32p, P, P, P, L,
                                     I, _c_i32p, _c_vpp, _c_i64p, _c_vpp, P, P, S, P]
     lib.lra_attn_decode.restype = ctypes.c_int
+    lib.lra_attn_decode_noalloc.argtypes = [ctypes.c_int, I, I, I, I, _c_i32p, _c_i32p, _c_i32p,
+                                            P, P, P, L, I, _c_i32p, _c_vpp, _c_i64p, _c_vpp, P,
+                                            P]
+    lib.lra_attn_decode_noalloc.restype = ctypes.c_int
     lib.lra_attn_workspace_bytes.argtypes = [ctypes.c_int, ctypes.c_int, I, _c_i32p, _c_i32p, I, I,
                                              I, I]
     lib.lra_attn_workspace_bytes.restype = ctypes.c_size_t
@@ -340,3 +345,37 @@ def lra_attn_decode(Q, K_base, V_base, L, B, k_start, k_len, agent_idx, O=None, 
     with torch.cuda.stream(stream) if stream is not None else _nullctx():
         return prepare_attn_decode(Q, K_base, V_base, L, B, k_start, k_len, agent_idx, O,
                                    workspace)(stream)
+
+
+def prepare_attn_decode_noalloc(Q, K_base, V_base, L, B, k_start, k_len, agent_idx, O):
+    """Prepared lra_attn_decode_noalloc: the decode with the library's fixed scratch; O is
+    the caller's output [batch, Hq, D] (nothing is allocated)."""
+    _dev(Q, "Q"), _dev(K_base, "K_base"), _dev(V_base, "V_base"), _dev(O, "O")
+    _like(K_base, Q, "K_base"), _like(V_base, Q, "V_base"), _like(O, Q, "O")
+    dt = _dtype(Q)
+    batch, Hq, D = Q.shape
+    kv_rows, Hkv, _ = K_base.shape
+    ranks = _adapter_ranks(Q, L, B, kv_rows, Hkv, D)
+    ks, ksp = _i32(k_start)
+    kl, klp = _i32(k_len)
+    ag, agp = _i32(agent_idx)
+    rk, rkp = _i32(ranks)
+    lk, lp = _ptrs(L)
+    ld, ldp = _i64([(l.stride(0) if l is not None else 0) for l in L])
+    bk, bp = _ptrs(B)
+    args = (dt, batch, Hq, Hkv, D, ksp, klp, agp, Q.data_ptr(), K_base.data_ptr(),
+            V_base.data_ptr(), kv_rows, len(rk), rkp, lp, ldp, bp, O.data_ptr(), None)
+    keep = (Q, K_base, V_base, L, B, O, ks, kl, ag, rk, lk, ld, bk)
+    return Prepared(lib.lra_attn_decode_noalloc, args, keep, O, 18)
+
+
+def lib_noalloc_scratch_bytes():
+    """Size of the library's fixed decode scratch (LRA_NOALLOC_SCRATCH_BYTES)."""
+    return NOALLOC_SCRATCH_BYTES
+
+
+def lra_attn_decode_noalloc(Q, K_base, V_base, L, B, k_start, k_len, agent_idx, O, stream=None):
+    """lra_attn_decode without a workspace: the split-key scratch is the library's fixed
+    per-GPU array (calls that may overlap on one GPU race on it)."""
+    return prepare_attn_decode_noalloc(Q, K_base, V_base, L, B, k_start, k_len, agent_idx,
+                                       O)(stream)
