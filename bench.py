@@ -20,6 +20,9 @@ flushed between calls of the HBM-bound ones):
   append      decode-step LR append: 64 new tokens x 4096 into 4 rank-16 caches (HBM GB/s)
   precompute  L = X·[A_1..A_3], X [32768, 4096], ranks 3 x 64              (HBM GB/s)
   longctx     512 queries over 32768 keys, rank 64, L from the precompute   (TFLOP/s)
+  naive_expansion  the regrouped kernels beside the naive route (V_full = V_base + L·B
+              materialised, then plain attention) and the in-tile expansion route, on the
+              Llama prefill, the decode batch and the long-context prefill
   mixed       32 layers of a 32-request batch, ranks 8/16/32/64 (--no-mixed skips it)
 and the CPU fp64 oracle timed on a bounded sample of the headline workload.
 
@@ -320,6 +323,77 @@ def bench_longctx(steps, warmup, flush):
     return precompute, longctx
 
 
+def bench_naive_expansion(steps, warmup, flush):
+    """The regrouped kernels against the two comparators of the regrouping, on the Llama
+    prefill, the decode batch and the long-context prefill (its LR caches from the
+    precompute): the naive route (lra_expand_values writes V_full = V_base + L·B, then plain
+    attention reads it) and the in-tile expansion route (each V tile expanded in LDS before
+    P·V).  Compute-bound prefills run back to back; the decode batch is timed with the
+    caches flushed before every call.  FLOP and bytes are what each route's LR term adds to
+    plain attention (accounting.lr_term_work)."""
+    import torch
+    from shared_rank_kv_amd import accounting, lra, workloads
+    out = {}
+    for key in ("llama_prefill", "decode", "longctx_prefill"):
+        if key == "llama_prefill":
+            prob = workloads.llama_prefill(agents=(0,))
+            _, dev = upload(prob)
+        elif key == "decode":
+            prob = workloads.decode_batch()
+            _, dev = upload(prob)
+        else:
+            pre = workloads.longctx_precompute()
+            X = pre.X().cuda()
+            A_cat = torch.cat([pre.A(a) for a in range(3)], 1).contiguous().cuda()
+            Ls = [torch.empty(pre.T, r, dtype=torch.bfloat16, device="cuda") for r in pre.ranks]
+            lra.lra_precompute_lr(X, A_cat, pre.ranks, Ls)
+            del X, A_cat
+            prob = workloads.longctx_prefill(agents=(0,))
+            _, dev = upload(prob, L=Ls)
+        decode = key == "decode"
+        ws = workspace_for(prob, decode)
+        zero = np.zeros(prob.batch, np.int32)
+        Vf = torch.empty_like(dev["V"])
+        expand = lra.prepare_expand_values(dev["V"], dev["L"], dev["B"], prob.k_start,
+                                           prob.k_len, prob.agent_idx, Vf)
+        if decode:
+            mk = lambda V, L, B, ag, ex=False: lra.prepare_attn_decode(  # noqa: E731
+                dev["Q"], dev["K"], V, L, B, prob.k_start, prob.k_len, ag,
+                O=torch.empty_like(dev["Q"]), workspace=ws, expand=ex)
+        else:
+            mk = lambda V, L, B, ag, ex=False: lra.prepare_attn_prefill(  # noqa: E731
+                dev["Q"], dev["K"], V, L, B, prob.q_start, prob.q_len, prob.k_start, prob.k_len,
+                ag, O=torch.empty_like(dev["Q"]), workspace=ws, expand=ex)
+        fla = mk(dev["V"], dev["L"], dev["B"], prob.agent_idx)
+        settle(fla)
+        plain = mk(Vf, [None], [None], zero)
+        intile = mk(dev["V"], dev["L"], dev["B"], prob.agent_idx, True)
+
+        def naive():
+            expand()
+            plain()
+        fl = flush if decode else None
+        ms = {}
+        for name, fn in (("regrouped", fla), ("naive", naive), ("naive_expand_only", expand),
+                         ("naive_attention_only", plain), ("in_tile", intile)):
+            per, _ = time_calls(fn, steps, warmup, fl)
+            ms[name] = float(np.median(per))
+        flop, nbytes = accounting.attention_work(prob)
+        work = {r: accounting.lr_term_work(prob, r) for r in ("regrouped", "naive", "in_tile")}
+        out[key] = {
+            "workload": prob.name, "ms": {k: round(v, 4) for k, v in ms.items()},
+            "regrouped_speedup_vs_naive": round(ms["naive"] / ms["regrouped"], 3),
+            "regrouped_speedup_vs_in_tile": round(ms["in_tile"] / ms["regrouped"], 3),
+            "expand_GBps": round(work["naive"][1] / (ms["naive_expand_only"] * 1e-3) / 1e9, 1),
+            "attention_flop": flop, "attention_bytes": nbytes,
+            "lr_term_flop": {k: v[0] for k, v in work.items()},
+            "lr_term_bytes": {k: v[1] for k, v in work.items()},
+        }
+        del dev, Vf, expand, fla, plain, intile
+        torch.cuda.empty_cache()
+    return out
+
+
 def bench_mixed(steps, warmup):
     import torch
     from shared_rank_kv_amd import accounting, lra, workloads
@@ -460,6 +534,8 @@ def run_only(args):
         return bench_decode_shared(args.steps, args.warmup, Flusher())
     if args.only == "append":
         return bench_append(args.steps, args.warmup, Flusher())
+    if args.only == "naive":
+        return bench_naive_expansion(args.steps, args.warmup, Flusher())
     if args.only == "longctx":
         pre, lc = bench_longctx(args.steps, args.warmup, Flusher())
         return {"precompute": pre, "longctx_prefill": lc}
@@ -475,7 +551,7 @@ def main():
                     help="time the 32-layer mixed batch (the default; kept for old command lines)")
     ap.add_argument("--no-mixed", action="store_true", help="skip the 32-layer mixed batch")
     ap.add_argument("--only", choices=["prefill", "decode", "decode_shared", "append", "longctx",
-                                       "mixed", "copy"],
+                                       "naive", "mixed", "copy"],
                     help="time one workload only (for profiling); prints its JSON object. "
                          "'copy' times a 1 GiB device copy, the reference for HBM counters")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -528,6 +604,8 @@ def main():
         out["append"] = bench_append(args.steps, args.warmup, flush)
         log("[bench] precompute + long-context prefill")
         out["precompute"], out["longctx_prefill"] = bench_longctx(args.steps, args.warmup, flush)
+        log("[bench] naive and in-tile expansion comparators")
+        out["naive_expansion"] = bench_naive_expansion(args.steps, args.warmup, flush)
         del flush
         torch.cuda.empty_cache()
         if not args.no_mixed:

@@ -178,6 +178,69 @@ int lra_attn_decode(int dtype, int32_t batch,
                     void* stream);
 
 /*
+ * Comparators of the regrouping (LRAgent summary, section "3. Flash-LoRA-Attention": the
+ * naive reconstruction expands the LR term V_lr·B to the full value width, work that
+ * scales with r·d_out per key, and keeps a full-width value cache per agent).  They give
+ * the same attention output by the ungrouped route, for measuring the regrouped kernels
+ * against; bf16 only (LRA_DTYPE_F32 is LRA_ERR_UNSUPPORTED).
+ *
+ * lra_expand_values -- the agent's full-width values, materialised:
+ *     V_full[s, g, :] = V_base[s, g, :] + L_a[s, :] · B_a[:, g*head_dim : (g+1)*head_dim]
+ * for every row s of span i, s in [start[i], start[i] + len[i]), with a = agent_idx[i],
+ * from fp32 accumulation rounded to bf16 (nearest even).  Rows outside the spans are left
+ * untouched.
+ *   start, len, agent_idx   host [n_spans]; spans must not overlap and lie in [0, kv_rows)
+ *   V_base, V_full          device [kv_rows, n_kv_heads, head_dim] (16-byte aligned);
+ *                           V_full may be V_base itself (in place), else must not overlap it
+ *   ranks, L, ldl, B        the adapters, as for lra_attn_prefill
+ * Plain attention over V_full (lra_attn_prefill / lra_attn_decode with rank-0 adapters)
+ * then completes the naive route.
+ */
+int lra_expand_values(int dtype, int32_t n_spans,
+                      const int32_t* start, const int32_t* len, const int32_t* agent_idx,
+                      const void* V_base, int64_t kv_rows,
+                      int32_t n_kv_heads, int32_t head_dim,
+                      int32_t n_agents, const int32_t* ranks,
+                      const void* const* L, const int64_t* ldl,
+                      const void* const* B,
+                      void* V_full,
+                      void* stream);
+
+/*
+ * lra_attn_prefill_expand, lra_attn_decode_expand -- the in-tile expansion route: the
+ * arguments, results and workspace of lra_attn_prefill / lra_attn_decode, but each tile of
+ * V_base rows is expanded to full width in on-chip memory, V_tile + L_tile·B_g (rounded to
+ * bf16), before P·V, instead of carrying P·L and applying B once per block of query rows.
+ * Requests are not grouped by shared context (one expanded tile serves one agent).
+ */
+int lra_attn_prefill_expand(int dtype, int32_t batch,
+                            int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                            const int32_t* q_start, const int32_t* q_len,
+                            const int32_t* k_start, const int32_t* k_len,
+                            const int32_t* agent_idx,
+                            const void* Q, int64_t q_rows,
+                            const void* K_base, const void* V_base, int64_t kv_rows,
+                            int32_t n_agents, const int32_t* ranks,
+                            const void* const* L, const int64_t* ldl,
+                            const void* const* B,
+                            void* O,
+                            void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+int lra_attn_decode_expand(int dtype, int32_t batch,
+                           int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                           const int32_t* k_start, const int32_t* k_len,
+                           const int32_t* agent_idx,
+                           const void* Q,
+                           const void* K_base, const void* V_base, int64_t kv_rows,
+                           int32_t n_agents, const int32_t* ranks,
+                           const void* const* L, const int64_t* ldl,
+                           const void* const* B,
+                           void* O,
+                           void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/*
  * lra_attn_decode_noalloc -- lra_attn_decode for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation):
  * the same arguments and results without `workspace`.  The split-key scratch is a fixed

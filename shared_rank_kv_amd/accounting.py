@@ -74,6 +74,50 @@ def attention_work_per_request(prob):
     return out
 
 
+def lr_term_work(prob, route, rows_per_tile=256, keys_per_tile=64):
+    """(flop, bytes) the LR term adds to plain attention on ``prob``, by route:
+    * "regrouped" (Flash-LoRA-Attention): 2*r per unmasked pair and q head (P·L) plus 2*r*D
+      per query row and q head ((P·L)·B); bytes: the LR rows and B;
+    * "naive": the expansion V_full = V_base + L·B of every key row of every request,
+      2*r*D*Hkv per row, before plain attention; bytes: V_base read, V_full written, the
+      LR rows and B (the plain attention then reads V_full instead of V_base);
+    * "in_tile": the same expansion repeated per work item inside the kernel: every key
+      tile a row tile of rows_per_tile (query, head) rows visits is expanded once, 2*r*D
+      per key per kv head; no bytes beyond the regrouped route's.
+    Rank-0 requests add nothing."""
+    e = _elem(prob.dtype)
+    D, Hq, Hkv = prob.head_dim, prob.n_q_heads, prob.n_kv_heads
+    G = Hq // Hkv
+    flop = nbytes = 0
+    agents = set()
+    for b in range(prob.batch):
+        lq, lk = int(prob.q_len[b]), int(prob.k_len[b])
+        r = prob.ranks[int(prob.agent_idx[b])]
+        if lq == 0 or r == 0:
+            continue
+        agents.add(int(prob.agent_idx[b]))
+        if route == "regrouped":
+            pairs = lq * (lk - lq) + lq * (lq + 1) // 2
+            flop += Hq * pairs * 2 * r + Hq * lq * 2 * r * D
+            nbytes += lk * r * e
+        elif route == "naive":
+            flop += lk * 2 * r * D * Hkv
+            nbytes += lk * Hkv * D * e * 2 + lk * r * e
+        elif route == "in_tile":
+            keys = 0
+            rows = lq * G
+            for r0 in range(0, rows, rows_per_tile):
+                last = min(r0 + rows_per_tile, rows) - 1
+                kend = lk - lq + last // G + 1
+                keys += -(-kend // keys_per_tile) * keys_per_tile if lq > 1 else lk
+            flop += Hkv * keys * 2 * r * D
+            nbytes += lk * r * e
+        else:
+            raise ValueError(route)
+    nbytes += sum(prob.ranks[a] * Hkv * D * e for a in agents)
+    return flop, nbytes
+
+
 def precompute_work(p):
     e = _elem(p.dtype)
     R = sum(p.ranks)

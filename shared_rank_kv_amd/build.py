@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(CSRC, "_build")
 LIB = os.path.join(PKG, "liblra.so")
 SOURCES = ["lra_api.cpp", "fla_bf16.hip", "fla_decode.hip", "fla_f32.hip", "precompute.hip",
-           "noalloc.hip"]
+           "noalloc.hip", "expand.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

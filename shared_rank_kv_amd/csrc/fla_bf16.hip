@@ -214,7 +214,13 @@ constexpr int kPfReads = 18;
 // LDS buffers rotate.  Each group issues part of the direct loads in its softmax phase:
 // group A the K rows, group B the V_base and L rows (see step).  The loop is unrolled by three so that every LDS access
 // names its buffer statically.
-template <int D, int RB>
+//
+// EX (the in-tile expansion comparator, not the regrouped path): group B expands every
+// V_base tile to full width in LDS, V_tile + L_tile·B_g, at the start of its matrix phase
+// M(j), and attention runs without an adapter term.  B then waits for V(j+1) at the end of
+// its softmax phase (three phases of latency, like K), so the tile is complete when the
+// expansion starts.
+template <int D, int RB, bool EX>
 __global__ __launch_bounds__(512, 1) void fla_prefill_bf16(const AttnArgs args) {
   const AttnArgs* A = (const AttnArgs*)__builtin_amdgcn_kernarg_segment_ptr();
   constexpr int DB = D / 32;
@@ -222,13 +228,16 @@ __global__ __launch_bounds__(512, 1) void fla_prefill_bf16(const AttnArgs args) 
   constexpr int TILE_KV = 64 * D * 2;
   constexpr int TILE_L = 64 * 64 * 2;
   constexpr int BUF = 2 * TILE_KV + (RB ? TILE_L : 0);
+  constexpr int RBA = EX ? 0 : RB;     // rank blocks of the attention's LR term
   constexpr int kRows = kPrefillRows;
   __shared__ __attribute__((aligned(1024))) char smem0[BUF];
   __shared__ __attribute__((aligned(1024))) char smem1[BUF];
   __shared__ __attribute__((aligned(1024))) char smem2[BUF];
+  __shared__ __attribute__((aligned(1024))) char smemb[EX ? TILE_KV : 16];
   LDS char* const buf0 = (LDS char*)smem0;
   LDS char* const buf1 = (LDS char*)smem1;
   LDS char* const buf2 = (LDS char*)smem2;
+  LDS char* const btile = (LDS char*)smemb;
 
   const int bid = blockIdx.x;
   const int w = A->grid_per_xcd > 0
@@ -318,11 +327,11 @@ __global__ __launch_bounds__(512, 1) void fla_prefill_bf16(const AttnArgs args) 
   };
 
   f32x16 accV[DB];
-  f32x16 accL[RB > 0 ? RB : 1];
+  f32x16 accL[RBA > 0 ? RBA : 1];
 #pragma unroll
   for (int i = 0; i < DB; ++i) accV[i] = f32x16{};
 #pragma unroll
-  for (int i = 0; i < (RB > 0 ? RB : 1); ++i) accL[i] = f32x16{};
+  for (int i = 0; i < (RBA > 0 ? RBA : 1); ++i) accL[i] = f32x16{};
   float m_run = kNegBig, l_run = 0.f;
   const float sl2 = A->scale_log2;
   f32x16 s[2];
@@ -340,12 +349,12 @@ __global__ __launch_bounds__(512, 1) void fla_prefill_bf16(const AttnArgs args) 
 #pragma unroll
         for (int db = 0; db < DB; ++db) accV[db] = mfma32(vfrag<D>(vt, off.v[db], key0), pf[st], accV[db]);
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) accL[rb] = mfma32(lfrag(lt, off.l[rb], key0), pf[st], accL[rb]);
+        for (int rb = 0; rb < RBA; ++rb) accL[rb] = mfma32(lfrag(lt, off.l[rb], key0), pf[st], accL[rb]);
       }
       // scheduling: kPfReads LDS reads first, then one MFMA per two further reads, so each
       // MFMA's operands were requested several MFMAs earlier (the compiler's own order kept
       // only one fragment in flight and the MFMAs waited on LDS latency)
-      constexpr int NR = 8 * DB + 8 * RB, NM = 4 * DB + 4 * RB;   // LDS reads, MFMAs
+      constexpr int NR = 8 * DB + 8 * RBA, NM = 4 * DB + 4 * RBA;   // LDS reads, MFMAs
       __builtin_amdgcn_sched_group_barrier(0x100, kPfReads, 0);
 #pragma unroll
       for (int i = 0; i < (NR - kPfReads) / 2; ++i) {
@@ -401,7 +410,7 @@ __global__ __launch_bounds__(512, 1) void fla_prefill_bf16(const AttnArgs args) 
 #pragma unroll
       for (int i = 0; i < DB; ++i) accV[i] *= alpha;
 #pragma unroll
-      for (int i = 0; i < RB; ++i) accL[i] *= alpha;
+      for (int i = 0; i < RBA; ++i) accL[i] *= alpha;
     }
     float psum = 0.f;
 #pragma unroll
@@ -416,6 +425,35 @@ __global__ __launch_bounds__(512, 1) void fla_prefill_bf16(const AttnArgs args) 
 #pragma unroll
     for (int st = 0; st < 4; ++st) pf[st] = pfrag(s[st >> 1], st & 1);
   };
+  // In-tile expansion of tile j (group B, EX): V_tile += L_tile·B_g as the MFMA product
+  // (L·B_g)ᵀ = B_gᵀ·Lᵀ.  B_g sits in btile in the V tile layout, so vfrag reads B_gᵀ with the
+  // same permuted k slots as the keys of Oᵀ += Vᵀ·Pᵀ; the L operand supplies ranks
+  // r0 + hi*4 + (0..3) and r0 + 8 + hi*4 + (0..3) of one key row.  Units are (32-lane head
+  // block, 32-key block); each B wave takes every fourth.
+  auto expand_tile = [&](LDS char* vt, const LDS char* lt) {
+    if (rank <= 0) return;
+    for (int u = wave & 3; u < DB * 2; u += 4) {
+      const int db = u % DB, key = (u / DB) * 32 + col;
+      const int lswap = ((key >> 1) & 1) * 64;
+      f32x16 c = f32x16{};
+      for (int r0 = 0; r0 < rank; r0 += 16) {
+        const i16x4 l0 = *(const LDS i16x4*)(lt + key * 128 + (((r0 + hi * 4) * 2) ^ lswap));
+        const i16x4 l1 = *(const LDS i16x4*)(lt + key * 128 + (((r0 + 8 + hi * 4) * 2) ^ lswap));
+        c = mfma32(vfrag<D>(btile, off.v[db], r0), join(l0, l1), c);
+      }
+      // lane holds key `key`, head lanes db*32 + 8*i + 4*hi .. +3
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d = db * 32 + i * 8 + hi * 4;
+        LDS char* vp = vt + key * (D * 2) + (((d >> 3) ^ swz_v<D>(key)) << 4) + (d & 7) * 2;
+        const bf16x4 vb = __builtin_bit_cast(bf16x4, *(LDS i16x4*)vp);
+        bf16x4 o;
+#pragma unroll
+        for (int j2 = 0; j2 < 4; ++j2) o[j2] = (bf16)((float)vb[j2] + c[i * 4 + j2]);
+        *(LDS bf16x4*)vp = o;
+      }
+    }
+  };
   // one step j of this wave's program (two barriers), buffers named statically.
   //  - K(t) is read in phases 2t and 2t+1; group A issues it as it enters V(t-2) (phase
   //    2t-3) and waits for it at the end of V(t-1): three phases of latency.
@@ -423,13 +461,14 @@ __global__ __launch_bounds__(512, 1) void fla_prefill_bf16(const AttnArgs args) 
   //    enters V(t-2) (phase 2t-2) and waits for them at the end of M(t): four phases.
   // Each wait leaves the next tile's loads in flight (vmcnt(N)), except where no next tile
   // was issued.  With the parts split, both softmax phases carry a share of the issue work.
-  auto step = [&](int j, const LDS char* kbuf, const LDS char* vbuf, LDS char* dma) {
+  auto step = [&](int j, LDS char* kbuf, const LDS char* vbuf, LDS char* dma) {
     // the matrix phase runs at raised wave priority so the SIMD's arbiter serves its
     // MFMA and LDS issue ahead of the partner wave's softmax
     __builtin_amdgcn_s_setprio(2);
+    if (EX && group_b && j < n_tiles) expand_tile(kbuf + TILE_KV, kbuf + 2 * TILE_KV);
     mma_phase(j, kbuf, vbuf);
     __builtin_amdgcn_s_setprio(0);
-    if (group_b) {                       // V(j) complete; V(j+1) may stay in flight
+    if (!EX && group_b) {                // V(j) complete; V(j+1) may stay in flight
       if (j + 1 < n_tiles) wait_loads_but<N_V>();
       else wait_loads();
     }
@@ -441,6 +480,9 @@ __global__ __launch_bounds__(512, 1) void fla_prefill_bf16(const AttnArgs args) 
     valu_phase(j);
     if (!group_b) {                      // K(j+1) complete; K(j+2) may stay in flight
       if (j + 2 < n_tiles) wait_loads_but<N_K>();
+      else wait_loads();
+    } else if (EX) {                     // V(j+1) complete; V(j+2) may stay in flight
+      if (j + 2 < n_tiles) wait_loads_but<N_V>();
       else wait_loads();
     }
     lds_barrier();
@@ -454,6 +496,12 @@ __global__ __launch_bounds__(512, 1) void fla_prefill_bf16(const AttnArgs args) 
     else wait_loads();
   } else {
     if (n_tiles > 0) load_vl(kb, buf0);
+    if (EX && rank > 0) {             // B_g as a 64-row value tile, rows past the rank zero
+      const auto br = rows_rsrc((const bf16*)AG.B + g * D, rank * row_bytes);
+#pragma unroll
+      for (int i = 0; i < TileLoader<D, 4>::UPW; ++i)
+        load_unit(br, btile + ((wave & 3) + 4 * i) * 1024, ld.voff[i]);
+    }
     wait_loads();
   }
   lds_barrier();
@@ -477,7 +525,7 @@ __global__ __launch_bounds__(512, 1) void fla_prefill_bf16(const AttnArgs args) 
 #pragma unroll
     for (int i = 0; i < DB; ++i) accV[i] *= inv;
   }
-  if (RB && rank > 0) {
+  if (RBA && rank > 0) {
     wait_loads();                 // nothing of the key loop is still in flight
     if (group_b) {
       const auto br = rows_rsrc((const bf16*)AG.B + g * D, rank * row_bytes);
@@ -607,18 +655,26 @@ __global__ __launch_bounds__(256) void fla_combine_bf16(const AttnArgs args) {
 }  // namespace
 
 hipError_t launch_prefill_bf16(const AttnArgs& a, int head_dim, int max_rank, int n_grid,
-                               hipStream_t s) {
+                               hipStream_t s, bool expand) {
   const int rb = max_rank > 32 ? 2 : (max_rank > 0 ? 1 : 0);
-#define LRA_LAUNCH(D, RB) \
-  hipLaunchKernelGGL((fla_prefill_bf16<D, RB>), dim3(n_grid), dim3(512), 0, s, a)
-  if (head_dim == 128) {
-    if (rb == 0) LRA_LAUNCH(128, 0);
-    else if (rb == 1) LRA_LAUNCH(128, 1);
-    else LRA_LAUNCH(128, 2);
+#define LRA_LAUNCH(D, RB, EX) \
+  hipLaunchKernelGGL((fla_prefill_bf16<D, RB, EX>), dim3(n_grid), dim3(512), 0, s, a)
+  if (expand && rb > 0) {
+    if (head_dim == 128) {
+      if (rb == 1) LRA_LAUNCH(128, 1, true);
+      else LRA_LAUNCH(128, 2, true);
+    } else {
+      if (rb == 1) LRA_LAUNCH(64, 1, true);
+      else LRA_LAUNCH(64, 2, true);
+    }
+  } else if (head_dim == 128) {
+    if (rb == 0) LRA_LAUNCH(128, 0, false);
+    else if (rb == 1) LRA_LAUNCH(128, 1, false);
+    else LRA_LAUNCH(128, 2, false);
   } else {
-    if (rb == 0) LRA_LAUNCH(64, 0);
-    else if (rb == 1) LRA_LAUNCH(64, 1);
-    else LRA_LAUNCH(64, 2);
+    if (rb == 0) LRA_LAUNCH(64, 0, false);
+    else if (rb == 1) LRA_LAUNCH(64, 1, false);
+    else LRA_LAUNCH(64, 2, false);
   }
 #undef LRA_LAUNCH
   return hipGetLastError();

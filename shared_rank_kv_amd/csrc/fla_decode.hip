@@ -26,6 +26,7 @@ namespace {
 
 typedef __bf16 bf16;
 typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
@@ -72,7 +73,11 @@ __device__ __forceinline__ float col_sum(float x) {
 template <int D>
 __device__ __forceinline__ int vswz(int k) { return D == 128 ? 2 * (k & 7) : 2 * ((k >> 1) & 3); }
 
-template <int D, int RB>
+// EX (the in-tile expansion comparator, not the regrouped path): every V_base tile is
+// expanded to full width in LDS, V_tile + L_tile·B_g, before P·V, and attention then runs
+// without an adapter term.  B_g stays in LDS for the whole work item; RB sizes its rank
+// steps.
+template <int D, int RB, bool EX>
 __global__ __launch_bounds__(256, 2) void fla_decode_bf16(const AttnArgs args) {
   const AttnArgs* A = (const AttnArgs*)__builtin_amdgcn_kernarg_segment_ptr();
   constexpr int CPR = D / 8;                 // 16-byte chunks per K/V row
@@ -81,10 +86,12 @@ __global__ __launch_bounds__(256, 2) void fla_decode_bf16(const AttnArgs args) {
   constexpr int VT = kKeys * D * 2;          // V tile bytes (per wave)
   constexpr int LT = kKeys * 64 * 2;         // LR tile bytes (per wave, rank <= 64)
   constexpr int VLOADS = VT / 1024;          // 16-byte V loads per lane per tile
-  constexpr int NRB = RB > 0 ? RB * 2 : 1;   // 16-column blocks of the LR accumulator
+  constexpr int RBA = EX ? 0 : RB;           // rank blocks of the attention's LR term
+  constexpr int NRB = RBA > 0 ? RBA * 2 : 1; // 16-column blocks of the LR accumulator
   constexpr int NL = RB == 2 ? 4 : 2;        // 16-byte L loads per lane per tile
   constexpr int NBU = D / 32;                // 16-byte units of a 64-row B tile per thread
-  __shared__ __attribute__((aligned(1024))) char smem_raw[4 * (VT + LT)];
+  constexpr int BT = EX ? 32 * RB * D * 2 : 0;   // B_g tile (in-tile expansion)
+  __shared__ __attribute__((aligned(1024))) char smem_raw[4 * (VT + LT) + BT];
   LDS char* smem = (LDS char*)smem_raw;
 
   const int bid = blockIdx.x;
@@ -219,10 +226,55 @@ __global__ __launch_bounds__(256, 2) void fla_decode_bf16(const AttnArgs args) {
   float m_run = kNegBig, l_run = 0.f;
   const float sl2 = A->scale_log2;
 
+  // In-tile expansion: B_g [32 RB rows (zero past the rank), D] in the V tile layout, read
+  // back transposed as the A operand of (L·B_g)ᵀ = B_gᵀ·Lᵀ, whose k slots are then the same
+  // permuted ranks as the keys of Oᵀ += Vᵀ·Pᵀ (see voff); the L operand supplies ranks
+  // kr*32 + grp*4 + (0..3) and kr*32 + 16 + grp*4 + (0..3) of one key row.
+  LDS char* bt = smem + 4 * (VT + LT);
+  if (EX) {
+    const bf16* Bg = rank > 0 ? (const bf16*)AG.B + g * D : nullptr;
+    for (int u = tid; u < 32 * RB * CPR; u += 256) {
+      const int row = u / CPR, c = u % CPR;
+      const u32x4 v = row < rank ? *(const u32x4*)(Bg + (int64_t)row * kv_stride + c * 8) : u32x4{};
+      *(LDS u32x4*)(bt + row * (D * 2) + ((c ^ vswz<D>(row)) << 4)) = v;
+    }
+    __syncthreads();
+  }
+  auto expand_tile = [&]() {
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      const int key = kb2 * 16 + col;
+      bf16x8 lf[RB > 0 ? RB : 1];
+#pragma unroll
+      for (int kr = 0; kr < RB; ++kr) {
+        const LDS char* p = lt + key * 128 + (kr * 32 + grp * 4) * 2;
+        lf[kr] = join(*(const LDS i16x4*)p, *(const LDS i16x4*)(p + 32));
+      }
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        f32x4 c = f32x4{};
+#pragma unroll
+        for (int kr = 0; kr < RB; ++kr)
+          c = mfma16(join(tr_read(bt + voff[db] + kr * 32 * D * 2),
+                          tr_read(bt + voff[db] + (kr * 32 + 16) * D * 2)), lf[kr], c);
+        // lane holds key `key`, head lanes db*16 + 4*grp .. +3
+        const int d = db * 16 + grp * 4;
+        LDS char* vp = vt + key * (D * 2) + (((d >> 3) ^ vswz<D>(key)) << 4) + (d & 7) * 2;
+        const i16x4 raw = *(LDS i16x4*)vp;
+        const bf16x4 vb = __builtin_bit_cast(bf16x4, raw);
+        bf16x4 o;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[j] = (bf16)((float)vb[j] + c[j]);
+        *(LDS bf16x4*)vp = o;
+      }
+    }
+  };
+
   if (my_tiles > 0) {
     load_k(0);
     load_vl(0);
     store_vl();
+    if (EX) expand_tile();
     load_vl(1);
     for (int jt = 0; jt < my_tiles; ++jt) {
       const int k0 = tile_key(jt);
@@ -271,7 +323,7 @@ __global__ __launch_bounds__(256, 2) void fla_decode_bf16(const AttnArgs args) {
       for (int db = 0; db < DB; ++db)
         acc[db] = mfma16(join(tr_read(vt + voff[db]), tr_read(vt + voff[db] + 16 * D * 2)), pf,
                          acc[db]);
-      if (RB) {
+      if (RBA) {
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb) {
           const LDS char* p = lt + trow * 128 + (rb * 16 + tq * 4) * 2;
@@ -281,6 +333,7 @@ __global__ __launch_bounds__(256, 2) void fla_decode_bf16(const AttnArgs args) {
       // the next tile's V and L replace this one: this wave's LDS reads above precede the
       // writes in program order, and the LDS executes one wave's operations in order
       store_vl();
+      if (EX) expand_tile();
       load_vl(jt + 2);
     }
   }
@@ -289,7 +342,7 @@ __global__ __launch_bounds__(256, 2) void fla_decode_bf16(const AttnArgs args) {
   const float l_col = col_sum(l_run);
   // B_g rows (rank x D, bf16) to registers now; their latency overlaps the merge
   u32x4 breg[NBU];
-  if (RB) {
+  if (RBA) {
     const bf16* Bg = (const bf16*)AG.B + g * D;
 #pragma unroll
     for (int i = 0; i < NBU; ++i) {
@@ -308,7 +361,7 @@ __global__ __launch_bounds__(256, 2) void fla_decode_bf16(const AttnArgs args) {
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int j = 0; j < 4; ++j) sh[(wave * 8 + col) * D + db * 16 + grp * 4 + j] = acc[db][j];
-    if (RB) {
+    if (RBA) {
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
@@ -319,7 +372,7 @@ __global__ __launch_bounds__(256, 2) void fla_decode_bf16(const AttnArgs args) {
       shm[(wave * 8 + col) * 2 + 1] = l_col;
     }
   }
-  if (RB) {
+  if (RBA) {
 #pragma unroll
     for (int i = 0; i < NBU; ++i) *(LDS u32x4*)(bs + (tid + 256 * i) * 16) = breg[i];
   }
@@ -337,7 +390,7 @@ __global__ __launch_bounds__(256, 2) void fla_decode_bf16(const AttnArgs args) {
       l += wgt[wv] * shm[(wv * 8 + c) * 2 + 1];
     }
   };
-  if (RB) {
+  if (RBA) {
     // merged P·L of every (column, rank index), columns past the rank hold zeros
 #pragma unroll
     for (int e = tid; e < 8 * 64; e += 256) {
@@ -368,9 +421,9 @@ __global__ __launch_bounds__(256, 2) void fla_decode_bf16(const AttnArgs args) {
       o0 += wgt[wv] * v[0];
       o1 += wgt[wv] * v[1];
     }
-    if (RB) {
+    if (RBA) {
 #pragma unroll
-      for (int rho = 0; rho < RB * 32; rho += 4) {
+      for (int rho = 0; rho < RBA * 32; rho += 4) {
         const f32x4 a = *(const LDS f32x4*)(sa + c * 64 + rho);
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -760,18 +813,26 @@ __global__ __launch_bounds__(256, RB == 2 ? 1 : 2) void fla_decode_shared_bf16(c
 }  // namespace
 
 hipError_t launch_decode_bf16(const AttnArgs& a, int head_dim, int max_rank, int n_grid,
-                              hipStream_t s) {
+                              hipStream_t s, bool expand) {
   const int rb = max_rank > 32 ? 2 : (max_rank > 0 ? 1 : 0);
-#define LRA_LAUNCH(D, RB) \
-  hipLaunchKernelGGL((fla_decode_bf16<D, RB>), dim3(n_grid), dim3(kThreads), 0, s, a)
-  if (head_dim == 128) {
-    if (rb == 0) LRA_LAUNCH(128, 0);
-    else if (rb == 1) LRA_LAUNCH(128, 1);
-    else LRA_LAUNCH(128, 2);
+#define LRA_LAUNCH(D, RB, EX) \
+  hipLaunchKernelGGL((fla_decode_bf16<D, RB, EX>), dim3(n_grid), dim3(kThreads), 0, s, a)
+  if (expand && rb > 0) {
+    if (head_dim == 128) {
+      if (rb == 1) LRA_LAUNCH(128, 1, true);
+      else LRA_LAUNCH(128, 2, true);
+    } else {
+      if (rb == 1) LRA_LAUNCH(64, 1, true);
+      else LRA_LAUNCH(64, 2, true);
+    }
+  } else if (head_dim == 128) {
+    if (rb == 0) LRA_LAUNCH(128, 0, false);
+    else if (rb == 1) LRA_LAUNCH(128, 1, false);
+    else LRA_LAUNCH(128, 2, false);
   } else {
-    if (rb == 0) LRA_LAUNCH(64, 0);
-    else if (rb == 1) LRA_LAUNCH(64, 1);
-    else LRA_LAUNCH(64, 2);
+    if (rb == 0) LRA_LAUNCH(64, 0, false);
+    else if (rb == 1) LRA_LAUNCH(64, 1, false);
+    else LRA_LAUNCH(64, 2, false);
   }
 #undef LRA_LAUNCH
   return hipGetLastError();

@@ -227,9 +227,11 @@ Plan make_plan(const AttnShape& s, bool decode, const int32_t* q_len, const int3
 // Dispatch
 // ---------------------------------------------------------------------------------------
 
+// expand: the in-tile expansion comparator instead of the regrouped LR term (bf16 only;
+// every request is its own work unit, since one expanded V tile serves one agent).
 int run_attention(const AttnShape& s, bool decode, const Requests& rq, const void* Q,
                   const void* K, const void* V, const Adapters& ad, void* O, void* ws,
-                  size_t ws_bytes, hipStream_t stream) {
+                  size_t ws_bytes, hipStream_t stream, bool expand = false) {
   const int32_t* q_len_arg = decode ? nullptr : rq.q_len;
   Plan p = make_plan(s, decode, q_len_arg, rq.k_len);
   if (p.active.empty()) return ok();
@@ -266,7 +268,7 @@ int run_attention(const AttnShape& s, bool decode, const Requests& rq, const voi
   // kMaxMembers (and 16 / G query columns) per unit, members consecutive in launch order;
   // every other request is a unit of its own.
   std::vector<int> unit_size(n, 1);
-  if (decode && s.dtype == LRA_DTYPE_BF16 && group_decode_enabled()) {
+  if (decode && s.dtype == LRA_DTYPE_BF16 && !expand && group_decode_enabled()) {
     const int cap = std::min(lra::kMaxMembers, 16 / G);
     bool fits = cap >= 2;
     for (size_t i = 0; i < n && fits; ++i) {
@@ -400,11 +402,11 @@ int run_attention(const AttnShape& s, bool decode, const Requests& rq, const voi
       int max_rank = 0;
       for (size_t i = c0; i < c1; ++i) max_rank = std::max(max_rank, ad.ranks[rq.agent[p.active[i]]]);
       if (!decode)
-        e = lra::launch_prefill_bf16(a, s.D, max_rank, grid, stream);
+        e = lra::launch_prefill_bf16(a, s.D, max_rank, grid, stream, expand);
       else if (shared)
         e = lra::launch_decode_shared_bf16(a, s.D, max_rank, grid, stream);
       else
-        e = lra::launch_decode_bf16(a, s.D, max_rank, grid, stream);
+        e = lra::launch_decode_bf16(a, s.D, max_rank, grid, stream, expand);
       if (e == hipSuccess && comb > 0) e = lra::launch_combine_bf16(a, s.D, stream);
     } else {
       a.grid_per_xcd = 0;
@@ -484,6 +486,64 @@ int check_lr_args(int dtype, int64_t T, int64_t d_model, const void* X, int64_t 
   return LRA_OK;
 }
 
+// The attention entry points; expand selects the in-tile expansion comparator.
+int attn_prefill_impl(bool expand, int dtype, int32_t batch, int32_t n_q_heads,
+                      int32_t n_kv_heads, int32_t head_dim, const int32_t* q_start,
+                      const int32_t* q_len, const int32_t* k_start, const int32_t* k_len,
+                      const int32_t* agent_idx, const void* Q, int64_t q_rows,
+                      const void* K_base, const void* V_base, int64_t kv_rows,
+                      int32_t n_agents, const int32_t* ranks, const void* const* L,
+                      const int64_t* ldl, const void* const* B, void* O, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  AttnShape s{dtype, batch, n_q_heads, n_kv_heads, head_dim};
+  int rc = check_shape(s);
+  if (rc) return rc;
+  if (expand && dtype != LRA_DTYPE_BF16)
+    return fail(LRA_ERR_UNSUPPORTED, "the in-tile expansion variant is bf16 only");
+  Adapters ad{n_agents, ranks, L, ldl, B};
+  if ((rc = check_adapters(dtype, ad, kv_rows))) return rc;
+  Requests rq{q_start, q_len, k_start, k_len, agent_idx};
+  if ((rc = check_requests(batch, rq, q_rows, kv_rows, n_agents))) return rc;
+  bool any = false;
+  for (int b = 0; b < batch; ++b) any |= q_len[b] > 0;
+  if (!any) return ok();
+  if (!Q || !K_base || !V_base || !O)
+    return fail(LRA_ERR_INVALID, "Q, K_base, V_base and O must be non-null");
+  if (!aligned(Q, 16) || !aligned(K_base, 16) || !aligned(V_base, 16) || !aligned(O, 16))
+    return fail(LRA_ERR_INVALID, "Q, K_base, V_base and O must be 16-byte aligned");
+  return run_attention(s, false, rq, Q, K_base, V_base, ad, O, workspace, workspace_bytes,
+                       (hipStream_t)stream, expand);
+}
+
+int attn_decode_impl(bool expand, int dtype, int32_t batch, int32_t n_q_heads,
+                     int32_t n_kv_heads, int32_t head_dim, const int32_t* k_start,
+                     const int32_t* k_len, const int32_t* agent_idx, const void* Q,
+                     const void* K_base, const void* V_base, int64_t kv_rows, int32_t n_agents,
+                     const int32_t* ranks, const void* const* L, const int64_t* ldl,
+                     const void* const* B, void* O, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  AttnShape s{dtype, batch, n_q_heads, n_kv_heads, head_dim};
+  int rc = check_shape(s);
+  if (rc) return rc;
+  if (expand && dtype != LRA_DTYPE_BF16)
+    return fail(LRA_ERR_UNSUPPORTED, "the in-tile expansion variant is bf16 only");
+  Adapters ad{n_agents, ranks, L, ldl, B};
+  if ((rc = check_adapters(dtype, ad, kv_rows))) return rc;
+  if (batch == 0) return ok();
+  if (!k_start || !k_len || !agent_idx)
+    return fail(LRA_ERR_INVALID, "request arrays must be non-null host arrays");
+  std::vector<int32_t> qs(batch), ql(batch, 1);
+  for (int b = 0; b < batch; ++b) qs[b] = b;
+  Requests rq{qs.data(), ql.data(), k_start, k_len, agent_idx};
+  if ((rc = check_requests(batch, rq, batch, kv_rows, n_agents))) return rc;
+  if (!Q || !K_base || !V_base || !O)
+    return fail(LRA_ERR_INVALID, "Q, K_base, V_base and O must be non-null");
+  if (!aligned(Q, 16) || !aligned(K_base, 16) || !aligned(V_base, 16) || !aligned(O, 16))
+    return fail(LRA_ERR_INVALID, "Q, K_base, V_base and O must be 16-byte aligned");
+  return run_attention(s, true, rq, Q, K_base, V_base, ad, O, workspace, workspace_bytes,
+                       (hipStream_t)stream, expand);
+}
+
 }  // namespace
 
 namespace lra {
@@ -515,22 +575,22 @@ int lra_attn_prefill(int dtype, int32_t batch, int32_t n_q_heads, int32_t n_kv_h
                      int64_t kv_rows, int32_t n_agents, const int32_t* ranks,
                      const void* const* L, const int64_t* ldl, const void* const* B, void* O,
                      void* workspace, size_t workspace_bytes, void* stream) {
-  AttnShape s{dtype, batch, n_q_heads, n_kv_heads, head_dim};
-  int rc = check_shape(s);
-  if (rc) return rc;
-  Adapters ad{n_agents, ranks, L, ldl, B};
-  if ((rc = check_adapters(dtype, ad, kv_rows))) return rc;
-  Requests rq{q_start, q_len, k_start, k_len, agent_idx};
-  if ((rc = check_requests(batch, rq, q_rows, kv_rows, n_agents))) return rc;
-  bool any = false;
-  for (int b = 0; b < batch; ++b) any |= q_len[b] > 0;
-  if (!any) return ok();
-  if (!Q || !K_base || !V_base || !O)
-    return fail(LRA_ERR_INVALID, "Q, K_base, V_base and O must be non-null");
-  if (!aligned(Q, 16) || !aligned(K_base, 16) || !aligned(V_base, 16) || !aligned(O, 16))
-    return fail(LRA_ERR_INVALID, "Q, K_base, V_base and O must be 16-byte aligned");
-  return run_attention(s, false, rq, Q, K_base, V_base, ad, O, workspace, workspace_bytes,
-                       (hipStream_t)stream);
+  return attn_prefill_impl(false, dtype, batch, n_q_heads, n_kv_heads, head_dim, q_start, q_len,
+                           k_start, k_len, agent_idx, Q, q_rows, K_base, V_base, kv_rows,
+                           n_agents, ranks, L, ldl, B, O, workspace, workspace_bytes, stream);
+}
+
+int lra_attn_prefill_expand(int dtype, int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                            int32_t head_dim, const int32_t* q_start, const int32_t* q_len,
+                            const int32_t* k_start, const int32_t* k_len,
+                            const int32_t* agent_idx, const void* Q, int64_t q_rows,
+                            const void* K_base, const void* V_base, int64_t kv_rows,
+                            int32_t n_agents, const int32_t* ranks, const void* const* L,
+                            const int64_t* ldl, const void* const* B, void* O, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  return attn_prefill_impl(true, dtype, batch, n_q_heads, n_kv_heads, head_dim, q_start, q_len,
+                           k_start, k_len, agent_idx, Q, q_rows, K_base, V_base, kv_rows,
+                           n_agents, ranks, L, ldl, B, O, workspace, workspace_bytes, stream);
 }
 
 int lra_attn_decode(int dtype, int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
@@ -539,24 +599,94 @@ int lra_attn_decode(int dtype, int32_t batch, int32_t n_q_heads, int32_t n_kv_he
                     const void* V_base, int64_t kv_rows, int32_t n_agents, const int32_t* ranks,
                     const void* const* L, const int64_t* ldl, const void* const* B, void* O,
                     void* workspace, size_t workspace_bytes, void* stream) {
-  AttnShape s{dtype, batch, n_q_heads, n_kv_heads, head_dim};
-  int rc = check_shape(s);
-  if (rc) return rc;
+  return attn_decode_impl(false, dtype, batch, n_q_heads, n_kv_heads, head_dim, k_start, k_len,
+                          agent_idx, Q, K_base, V_base, kv_rows, n_agents, ranks, L, ldl, B, O,
+                          workspace, workspace_bytes, stream);
+}
+
+int lra_attn_decode_expand(int dtype, int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                           int32_t head_dim, const int32_t* k_start, const int32_t* k_len,
+                           const int32_t* agent_idx, const void* Q, const void* K_base,
+                           const void* V_base, int64_t kv_rows, int32_t n_agents,
+                           const int32_t* ranks, const void* const* L, const int64_t* ldl,
+                           const void* const* B, void* O, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  return attn_decode_impl(true, dtype, batch, n_q_heads, n_kv_heads, head_dim, k_start, k_len,
+                          agent_idx, Q, K_base, V_base, kv_rows, n_agents, ranks, L, ldl, B, O,
+                          workspace, workspace_bytes, stream);
+}
+
+int lra_expand_values(int dtype, int32_t n_spans, const int32_t* start, const int32_t* len,
+                      const int32_t* agent_idx, const void* V_base, int64_t kv_rows,
+                      int32_t n_kv_heads, int32_t head_dim, int32_t n_agents,
+                      const int32_t* ranks, const void* const* L, const int64_t* ldl,
+                      const void* const* B, void* V_full, void* stream) {
+  if (dtype != LRA_DTYPE_BF16 && dtype != LRA_DTYPE_F32)
+    return fail(LRA_ERR_INVALID, "dtype %d is neither LRA_DTYPE_F32 nor LRA_DTYPE_BF16", dtype);
+  if (dtype != LRA_DTYPE_BF16) return fail(LRA_ERR_UNSUPPORTED, "lra_expand_values is bf16 only");
+  if (n_spans < 0) return fail(LRA_ERR_INVALID, "n_spans %d < 0", n_spans);
+  if (n_spans > LRA_MAX_BATCH)
+    return fail(LRA_ERR_UNSUPPORTED, "n_spans %d > LRA_MAX_BATCH (%d)", n_spans, LRA_MAX_BATCH);
+  if (n_kv_heads <= 0) return fail(LRA_ERR_INVALID, "n_kv_heads %d <= 0", n_kv_heads);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(LRA_ERR_UNSUPPORTED, "head_dim %d not in {64, 128}", head_dim);
   Adapters ad{n_agents, ranks, L, ldl, B};
-  if ((rc = check_adapters(dtype, ad, kv_rows))) return rc;
-  if (batch == 0) return ok();
-  if (!k_start || !k_len || !agent_idx)
-    return fail(LRA_ERR_INVALID, "request arrays must be non-null host arrays");
-  std::vector<int32_t> qs(batch), ql(batch, 1);
-  for (int b = 0; b < batch; ++b) qs[b] = b;
-  Requests rq{qs.data(), ql.data(), k_start, k_len, agent_idx};
-  if ((rc = check_requests(batch, rq, batch, kv_rows, n_agents))) return rc;
-  if (!Q || !K_base || !V_base || !O)
-    return fail(LRA_ERR_INVALID, "Q, K_base, V_base and O must be non-null");
-  if (!aligned(Q, 16) || !aligned(K_base, 16) || !aligned(V_base, 16) || !aligned(O, 16))
-    return fail(LRA_ERR_INVALID, "Q, K_base, V_base and O must be 16-byte aligned");
-  return run_attention(s, true, rq, Q, K_base, V_base, ad, O, workspace, workspace_bytes,
-                       (hipStream_t)stream);
+  int rc = check_adapters(dtype, ad, kv_rows);
+  if (rc) return rc;
+  if (n_spans == 0) return ok();
+  if (!start || !len || !agent_idx)
+    return fail(LRA_ERR_INVALID, "span arrays must be non-null host arrays");
+  std::vector<std::pair<int64_t, int64_t>> rows;
+  for (int i = 0; i < n_spans; ++i) {
+    if (start[i] < 0 || len[i] < 0 || (int64_t)start[i] + len[i] > kv_rows)
+      return fail(LRA_ERR_INVALID, "span %d: rows [%d, %lld) outside [0, %lld)", i, start[i],
+                  (long long)start[i] + len[i], (long long)kv_rows);
+    if (agent_idx[i] < 0 || agent_idx[i] >= n_agents)
+      return fail(LRA_ERR_INVALID, "span %d: agent_idx %d outside [0, %d)", i, agent_idx[i],
+                  n_agents);
+    if (len[i] > 0) rows.emplace_back(start[i], (int64_t)start[i] + len[i]);
+  }
+  std::sort(rows.begin(), rows.end());
+  for (size_t i = 1; i < rows.size(); ++i)
+    if (rows[i].first < rows[i - 1].second)
+      return fail(LRA_ERR_INVALID, "two spans overlap at row %lld", (long long)rows[i].first);
+  if (rows.empty()) return ok();
+  if (!V_base || !V_full) return fail(LRA_ERR_INVALID, "V_base and V_full must be non-null");
+  if (!aligned(V_base, 16) || !aligned(V_full, 16))
+    return fail(LRA_ERR_INVALID, "V_base and V_full must be 16-byte aligned");
+  lra::ExpandArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.V = V_base;
+  a.Vout = V_full;
+  a.Hkv = n_kv_heads;
+  for (int i = 0; i < n_agents; ++i) {
+    a.agents[i].L = L[i];
+    a.agents[i].B = B[i];
+    a.agents[i].ldl = ldl[i];
+    a.agents[i].rank = ranks[i];
+  }
+  int i0 = 0;
+  while (i0 < n_spans) {
+    int64_t work = 0;
+    int n = 0, max_rank = 0;
+    for (; i0 < n_spans && n < lra::kReqsPerLaunch; ++i0) {
+      if (len[i0] == 0) continue;
+      lra::ExpandSpan& sp = a.spans[n++];
+      sp.start = start[i0];
+      sp.len = len[i0];
+      sp.agent = agent_idx[i0];
+      sp.work_start = (int)work;
+      work += ceil_div(len[i0], lra::kExpandRows) * n_kv_heads;
+      max_rank = std::max(max_rank, ranks[agent_idx[i0]]);
+    }
+    if (n == 0) break;
+    if (work > INT32_MAX / 2) return fail(LRA_ERR_UNSUPPORTED, "launch too large");
+    a.n_span = n;
+    a.n_work = (int)work;
+    hipError_t e = lra::launch_expand_bf16(a, head_dim, max_rank, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(LRA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  }
+  return ok();
 }
 
 int lra_precompute_lr(int dtype, int64_t T, int64_t d_model, const void* X, int64_t ldx,

@@ -97,21 +97,40 @@ struct AppendArgs {
   int32_t rows[kAppendRows];
 };
 
+// Naive value expansion (the comparator of the regrouped kernels): span i covers rows
+// [start, start + len) of V_base, expanded with agent `agent`'s L and B into the same rows
+// of V_full.  Work items: (chunk of kExpandRows rows, kv head) with the kv head fastest.
+constexpr int kExpandRows = 512;
+struct ExpandSpan {
+  int64_t start;
+  int32_t len, agent, work_start, pad_;
+};
+struct ExpandArgs {
+  const void* V;
+  void* Vout;
+  int32_t Hkv, n_span, n_work, pad_;
+  AgentDesc agents[kMaxAgents];
+  ExpandSpan spans[kReqsPerLaunch];
+};
+
 // Sets the calling thread's lra_last_error() message and returns `code`.
 int report_error(int code, const char* msg);
 
 // Launchers (return the HIP status of the launch).
 hipError_t launch_prefill_bf16(const AttnArgs& a, int head_dim, int max_rank, int n_grid,
-                               hipStream_t s);
+                               hipStream_t s, bool expand = false);
 hipError_t launch_decode_shared_bf16(const AttnArgs& a, int head_dim, int max_rank, int n_grid,
                                      hipStream_t s);
+// expand: the in-tile expansion comparator (each V_base tile expanded with L·B_g in LDS
+// before P·V) instead of the regrouped LR term.
 hipError_t launch_decode_bf16(const AttnArgs& a, int head_dim, int max_rank, int n_grid,
-                              hipStream_t s);
+                              hipStream_t s, bool expand = false);
 hipError_t launch_combine_bf16(const AttnArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgs& a, int head_dim, int n_blocks, hipStream_t s);
 hipError_t launch_precompute_bf16(const PrecomputeArgs& a, hipStream_t s);
 hipError_t launch_precompute_f32(const PrecomputeArgs& a, hipStream_t s);
 hipError_t launch_append_bf16(const AppendArgs& a, hipStream_t s);
 hipError_t launch_append_f32(const AppendArgs& a, hipStream_t s);
+hipError_t launch_expand_bf16(const ExpandArgs& a, int head_dim, int max_rank, hipStream_t s);
 
 }  // namespace lra

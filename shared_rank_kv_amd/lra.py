@@ -22,6 +22,7 @@ LRA_OK, LRA_ERR_INVALID, LRA_ERR_UNSUPPORTED, LRA_ERR_WORKSPACE, LRA_ERR_HIP = r
 LRA_DTYPE_F32, LRA_DTYPE_BF16 = 0, 1
 NOALLOC_SCRATCH_BYTES = 32 << 20      # LRA_NOALLOC_SCRATCH_BYTES of include/lra.h
 SYMBOLS = ("lra_precompute_lr", "lra_append_lr", "lra_attn_prefill", "lra_attn_decode",
+           "lra_expand_values", "lra_attn_prefill_expand", "lra_attn_decode_expand",
            "lra_attn_decode_noalloc", "lra_attn_workspace_bytes", "lra_last_error")
 
 _c_i32p = ctypes.POINTER(ctypes.c_int32)
@@ -52,6 +53,13 @@ def _load():
     lib.lra_attn_decode.argtypes = [ctypes.c_int, I, I, I, I, _c_i32p, _c_i32p, _c_i32p, P, P, P, L,
                                     I, _c_i32p, _c_vpp, _c_i64p, _c_vpp, P, P, S, P]
     lib.lra_attn_decode.restype = ctypes.c_int
+    lib.lra_attn_prefill_expand.argtypes = lib.lra_attn_prefill.argtypes
+    lib.lra_attn_prefill_expand.restype = ctypes.c_int
+    lib.lra_attn_decode_expand.argtypes = lib.lra_attn_decode.argtypes
+    lib.lra_attn_decode_expand.restype = ctypes.c_int
+    lib.lra_expand_values.argtypes = [ctypes.c_int, I, _c_i32p, _c_i32p, _c_i32p, P, L, I, I, I,
+                                      _c_i32p, _c_vpp, _c_i64p, _c_vpp, P, P]
+    lib.lra_expand_values.restype = ctypes.c_int
     lib.lra_attn_decode_noalloc.argtypes = [ctypes.c_int, I, I, I, I, _c_i32p, _c_i32p, _c_i32p,
                                             P, P, P, L, I, _c_i32p, _c_vpp, _c_i64p, _c_vpp, P,
                                             P]
@@ -263,8 +271,9 @@ def lra_append_lr(X, A_cat, ranks, L_out, rows, stream=None):
 
 
 def prepare_attn_prefill(Q, K_base, V_base, L, B, q_start, q_len, k_start, k_len, agent_idx,
-                         O=None, workspace=None):
-    """Prepared lra_attn_prefill (see lra_attn_prefill)."""
+                         O=None, workspace=None, expand=False):
+    """Prepared lra_attn_prefill (see lra_attn_prefill); expand=True prepares the in-tile
+    expansion comparator lra_attn_prefill_expand instead."""
     _dev(Q, "Q"), _dev(K_base, "K_base"), _dev(V_base, "V_base")
     _like(K_base, Q, "K_base"), _like(V_base, Q, "V_base")
     dt = _dtype(Q)
@@ -292,7 +301,8 @@ def prepare_attn_prefill(Q, K_base, V_base, L, B, q_start, q_len, k_start, k_len
             O.data_ptr(), ws.data_ptr() if ws is not None else None, ws_bytes, None)
     keep = (Q, K_base, V_base, L, B, O, ws, qs, ql, ks, kl, ag, rk, lk, ld, bk)
     owned = (O if owned_O else None, ws if workspace is None else None)
-    return Prepared(lib.lra_attn_prefill, args, keep, O, 23, owned)
+    cfn = lib.lra_attn_prefill_expand if expand else lib.lra_attn_prefill
+    return Prepared(cfn, args, keep, O, 23, owned)
 
 
 def lra_attn_prefill(Q, K_base, V_base, L, B, q_start, q_len, k_start, k_len, agent_idx, O=None,
@@ -308,8 +318,9 @@ def lra_attn_prefill(Q, K_base, V_base, L, B, q_start, q_len, k_start, k_len, ag
 
 
 def prepare_attn_decode(Q, K_base, V_base, L, B, k_start, k_len, agent_idx, O=None,
-                        workspace=None):
-    """Prepared lra_attn_decode (see lra_attn_decode)."""
+                        workspace=None, expand=False):
+    """Prepared lra_attn_decode (see lra_attn_decode); expand=True prepares the in-tile
+    expansion comparator lra_attn_decode_expand instead."""
     _dev(Q, "Q"), _dev(K_base, "K_base"), _dev(V_base, "V_base")
     _like(K_base, Q, "K_base"), _like(V_base, Q, "V_base")
     dt = _dtype(Q)
@@ -335,7 +346,8 @@ def prepare_attn_decode(Q, K_base, V_base, L, B, k_start, k_len, agent_idx, O=No
             ws.data_ptr() if ws is not None else None, ws_bytes, None)
     keep = (Q, K_base, V_base, L, B, O, ws, ks, kl, ag, rk, lk, ld, bk)
     owned = (O if owned_O else None, ws if workspace is None else None)
-    return Prepared(lib.lra_attn_decode, args, keep, O, 20, owned)
+    cfn = lib.lra_attn_decode_expand if expand else lib.lra_attn_decode
+    return Prepared(cfn, args, keep, O, 20, owned)
 
 
 def lra_attn_decode(Q, K_base, V_base, L, B, k_start, k_len, agent_idx, O=None, workspace=None,
@@ -379,3 +391,58 @@ def lra_attn_decode_noalloc(Q, K_base, V_base, L, B, k_start, k_len, agent_idx, 
     per-GPU array (calls that may overlap on one GPU race on it)."""
     return prepare_attn_decode_noalloc(Q, K_base, V_base, L, B, k_start, k_len, agent_idx,
                                        O)(stream)
+
+
+# ---------------------------------------------------------------------------------------
+# comparators of the regrouping (naive expansion, in-tile expansion)
+# ---------------------------------------------------------------------------------------
+
+def lra_attn_prefill_expand(Q, K_base, V_base, L, B, q_start, q_len, k_start, k_len,
+                            agent_idx, O=None, workspace=None, stream=None):
+    """The in-tile expansion route of lra_attn_prefill (same arguments and result)."""
+    with torch.cuda.stream(stream) if stream is not None else _nullctx():
+        return prepare_attn_prefill(Q, K_base, V_base, L, B, q_start, q_len, k_start, k_len,
+                                    agent_idx, O, workspace, expand=True)(stream)
+
+
+def lra_attn_decode_expand(Q, K_base, V_base, L, B, k_start, k_len, agent_idx, O=None,
+                           workspace=None, stream=None):
+    """The in-tile expansion route of lra_attn_decode (same arguments and result)."""
+    with torch.cuda.stream(stream) if stream is not None else _nullctx():
+        return prepare_attn_decode(Q, K_base, V_base, L, B, k_start, k_len, agent_idx, O,
+                                   workspace, expand=True)(stream)
+
+
+def prepare_expand_values(V_base, L, B, start, length, agent_idx, V_full):
+    """Prepared lra_expand_values: V_full[s] <- V_base[s] + L_a[s]·B_a over the spans."""
+    _dev(V_base, "V_base"), _dev(V_full, "V_full")
+    _like(V_full, V_base, "V_full")
+    if V_full.shape != V_base.shape:
+        raise ValueError(f"V_full {tuple(V_full.shape)} must have V_base's shape "
+                         f"{tuple(V_base.shape)}")
+    kv_rows, Hkv, D = V_base.shape
+    ranks = _adapter_ranks(V_base, L, B, kv_rows, Hkv, D)
+    st, stp = _i32(start)
+    ln, lnp = _i32(length)
+    ag, agp = _i32(agent_idx)
+    rk, rkp = _i32(ranks)
+    lk, lp = _ptrs(L)
+    ld, ldp = _i64([(l.stride(0) if l is not None else 0) for l in L])
+    bk, bp = _ptrs(B)
+    args = (_dtype(V_base), len(st), stp, lnp, agp, V_base.data_ptr(), kv_rows, Hkv, D,
+            len(rk), rkp, lp, ldp, bp, V_full.data_ptr(), None)
+    keep = (V_base, L, B, V_full, st, ln, ag, rk, lk, ld, bk)
+    return Prepared(lib.lra_expand_values, args, keep, V_full, 15)
+
+
+def lra_expand_values(V_base, L, B, start, length, agent_idx, V_full=None, stream=None):
+    """The naive reconstruction: V_full[s] = V_base[s] + L_a[s]·B_a for the rows of every span
+    (rows outside the spans are left as they are; a new V_full starts uninitialised)."""
+    with torch.cuda.stream(stream) if stream is not None else _nullctx():
+        owned = V_full is None
+        if owned:
+            V_full = torch.empty_like(V_base)
+        p = prepare_expand_values(V_base, L, B, start, length, agent_idx, V_full)
+        if owned:
+            p._owned = (V_full,)
+        return p(stream)

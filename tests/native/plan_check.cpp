@@ -16,14 +16,16 @@
 #include "lra.h"
 #include "lra_internal.h"
 
-struct Rec { lra::AttnArgs a; int kind; int grid; };   // 0 prefill, 1 decode, 2 decode shared, 3 combine, 4 f32
+struct Rec { lra::AttnArgs a; int kind; int grid; bool expand; };   // 0 prefill, 1 decode, 2 decode shared, 3 combine, 4 f32
 static std::vector<Rec> g_recs;
+static std::vector<lra::ExpandArgs> g_expand;
 namespace lra {
-hipError_t launch_prefill_bf16(const AttnArgs& a, int, int, int grid, hipStream_t) { g_recs.push_back({a, 0, grid}); return hipSuccess; }
-hipError_t launch_decode_bf16(const AttnArgs& a, int, int, int, hipStream_t) { g_recs.push_back({a, 1, 0}); return hipSuccess; }
-hipError_t launch_decode_shared_bf16(const AttnArgs& a, int, int, int, hipStream_t) { g_recs.push_back({a, 2, 0}); return hipSuccess; }
-hipError_t launch_combine_bf16(const AttnArgs& a, int, hipStream_t) { g_recs.push_back({a, 3, 0}); return hipSuccess; }
-hipError_t launch_attn_f32(const AttnArgs& a, int, int, hipStream_t) { g_recs.push_back({a, 4, 0}); return hipSuccess; }
+hipError_t launch_prefill_bf16(const AttnArgs& a, int, int, int grid, hipStream_t, bool ex) { g_recs.push_back({a, 0, grid, ex}); return hipSuccess; }
+hipError_t launch_decode_bf16(const AttnArgs& a, int, int, int, hipStream_t, bool ex) { g_recs.push_back({a, 1, 0, ex}); return hipSuccess; }
+hipError_t launch_expand_bf16(const ExpandArgs& a, int, int, hipStream_t) { g_expand.push_back(a); return hipSuccess; }
+hipError_t launch_decode_shared_bf16(const AttnArgs& a, int, int, int, hipStream_t) { g_recs.push_back({a, 2, 0, false}); return hipSuccess; }
+hipError_t launch_combine_bf16(const AttnArgs& a, int, hipStream_t) { g_recs.push_back({a, 3, 0, false}); return hipSuccess; }
+hipError_t launch_attn_f32(const AttnArgs& a, int, int, hipStream_t) { g_recs.push_back({a, 4, 0, false}); return hipSuccess; }
 hipError_t launch_precompute_bf16(const PrecomputeArgs&, hipStream_t) { return hipSuccess; }
 hipError_t launch_precompute_f32(const PrecomputeArgs&, hipStream_t) { return hipSuccess; }
 hipError_t launch_append_bf16(const AppendArgs&, hipStream_t) { return hipSuccess; }
@@ -230,8 +232,67 @@ static void check_validation() {
                          outs, ldl, rows, 100, nullptr), LRA_OK, "valid append"); }
 }
 
+// The comparators: the in-tile expansion decode never groups shared contexts and launches
+// the expanding kernel; lra_expand_values splits spans into chunks of kExpandRows per kv
+// head, at most kReqsPerLaunch spans per launch, and refuses overlapping spans.
+static void check_comparators() {
+  std::vector<int> ks(8, 0), kl(8, 4096), ag = {0, 1, 0, 1, 0, 1, 0, 1};
+  const int ranks[2] = {16, 64};
+  const void* L[2] = {(void*)0x100000, (void*)0x200000};
+  const void* B[2] = {(void*)0x300000, (void*)0x400000};
+  const int64_t ldl[2] = {16, 64};
+  const size_t wsb = lra_attn_workspace_bytes(LRA_DTYPE_BF16, 1, 8, nullptr, kl.data(), 32, 8, 128, 64);
+  g_recs.clear();
+  expect(lra_attn_decode_expand(LRA_DTYPE_BF16, 8, 32, 8, 128, ks.data(), kl.data(), ag.data(),
+                                (void*)0x1000, (void*)0x2000, (void*)0x3000, 4096, 2, ranks, L,
+                                ldl, B, (void*)0x4000, (void*)0x10000000, wsb, nullptr),
+         LRA_OK, "decode, in-tile expansion");
+  bool any = false;
+  for (const Rec& r : g_recs) {
+    assert(r.kind != 2);
+    if (r.kind == 1) { assert(r.expand); any = true; }
+  }
+  assert(any);
+  expect(lra_attn_decode_expand(LRA_DTYPE_F32, 8, 32, 8, 128, ks.data(), kl.data(), ag.data(),
+                                (void*)0x1000, (void*)0x2000, (void*)0x3000, 4096, 2, ranks, L,
+                                ldl, B, (void*)0x4000, (void*)0x10000000, wsb, nullptr),
+         LRA_ERR_UNSUPPORTED, "in-tile expansion in fp32");
+  // 70 spans (two launches), one empty, lengths around the chunk size
+  std::vector<int> st, ln, sa;
+  int row = 0;
+  for (int i = 0; i < 70; ++i) {
+    const int n = i == 5 ? 0 : 1 + (i * 397) % 1500;
+    st.push_back(row); ln.push_back(n); sa.push_back(i % 2); row += n + (i % 3);
+  }
+  g_expand.clear();
+  expect(lra_expand_values(LRA_DTYPE_BF16, 70, st.data(), ln.data(), sa.data(), (void*)0x1000, row,
+                           8, 128, 2, ranks, L, ldl, B, (void*)0x2000, nullptr),
+         LRA_OK, "expand values");
+  assert(g_expand.size() == 2);
+  int seen = 0;
+  for (const lra::ExpandArgs& a : g_expand) {
+    int64_t work = 0;
+    for (int i = 0; i < a.n_span; ++i) {
+      const lra::ExpandSpan& sp = a.spans[i];
+      assert(sp.len > 0 && sp.work_start == work);
+      work += (int64_t)((sp.len + lra::kExpandRows - 1) / lra::kExpandRows) * 8;
+      ++seen;
+    }
+    assert(work == a.n_work && a.n_span <= lra::kReqsPerLaunch);
+  }
+  assert(seen == 69);
+  st[3] = st[2] + 1;   // overlaps span 2
+  expect(lra_expand_values(LRA_DTYPE_BF16, 70, st.data(), ln.data(), sa.data(), (void*)0x1000, row,
+                           8, 128, 2, ranks, L, ldl, B, (void*)0x2000, nullptr),
+         LRA_ERR_INVALID, "overlapping spans");
+  expect(lra_expand_values(LRA_DTYPE_F32, 1, st.data(), ln.data(), sa.data(), (void*)0x1000, row,
+                           8, 128, 2, ranks, L, ldl, B, (void*)0x2000, nullptr),
+         LRA_ERR_UNSUPPORTED, "expand values in fp32");
+}
+
 int main() {
   check_validation();
+  check_comparators();
   // prefill: a mixed batch (one launch), 100 requests (two launches), one request
   {
     std::vector<int> ql, kl;
