@@ -537,6 +537,8 @@ def run_only(args):
         return bench_decode_shared(args.steps, args.warmup, Flusher())
     if args.only == "append":
         return bench_append(args.steps, args.warmup, Flusher())
+    if args.only == "tiny":
+        return bench_tiny_fp32(args.steps, args.warmup)
     if args.only == "naive":
         return bench_naive_expansion(args.steps, args.warmup, Flusher())
     if args.only == "longctx":
@@ -553,8 +555,8 @@ def main():
     ap.add_argument("--mixed", action="store_true",
                     help="time the 32-layer mixed batch (the default; kept for old command lines)")
     ap.add_argument("--no-mixed", action="store_true", help="skip the 32-layer mixed batch")
-    ap.add_argument("--only", choices=["prefill", "decode", "decode_shared", "append", "longctx",
-                                       "naive", "mixed", "copy"],
+    ap.add_argument("--only", choices=["prefill", "tiny", "decode", "decode_shared", "append",
+                                       "longctx", "naive", "mixed", "copy"],
                     help="time one workload only (for profiling); prints its JSON object. "
                          "'copy' times a 1 GiB device copy, the reference for HBM counters")
     ap.add_argument("--no-cpu-baseline", action="store_true")

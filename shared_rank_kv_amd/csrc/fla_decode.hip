@@ -456,7 +456,10 @@ __global__ __launch_bounds__(256, 2) void fla_decode_bf16(const AttnArgs args) {
 // member: every tile, each member's L rows pass through the wave's LR tile in turn and
 // (P·L_a)ᵀ += L_aᵀ·Pᵀ runs with P masked to that member's columns, so one accumulator
 // holds, in every column, the product with that column's own agent.  B_a is applied per
-// member when the wave states are merged.
+// member when the wave states are merged.  Members may have seen different lengths of the
+// context (same first row): the first member is the longest and sets the key range, and
+// each column's scores are masked past its own member's length (a split past it leaves
+// that member the empty state, which the combine pass weighs zero).
 // (Ranks up to 32 keep two workgroups per CU, with a few registers spilled outside the key
 // loop; rank 64 needs the register file of one.)
 template <int D, int RB>
@@ -495,6 +498,8 @@ __global__ __launch_bounds__(256, RB == 2 ? 1 : 2) void fla_decode_shared_bf16(c
   const int col = lane & 15, grp = lane >> 4;
   const int mcol = col / G;                  // member of this lane's query column
   const bool col_ok = mcol < nm;
+  // keys of this lane's member: the first member is the longest, the others see a prefix
+  const int my_len = col_ok ? A->reqs[b + mcol].k_len : Lk;
 
   // key range of this split, in 32-key tiles dealt round-robin to the 4 waves
   const int n_tiles_req = (Lk + kKeys - 1) / kKeys;
@@ -540,7 +545,7 @@ __global__ __launch_bounds__(256, RB == 2 ? 1 : 2) void fla_decode_shared_bf16(c
       const AgentDesc& AG = A->agents[A->reqs[b + m].agent];
       if (AG.rank > 0) {
         base = (const bf16*)AG.L + (int64_t)k_start * AG.ldl;
-        bytes = (int)((int64_t)Lk * AG.ldl * 2);
+        bytes = (int)((int64_t)A->reqs[b + m].k_len * AG.ldl * 2);   // the member's own rows
         ldl_b[m] = (int)(AG.ldl * 2);
         rank_m[m] = AG.rank;
       }
@@ -642,7 +647,7 @@ __global__ __launch_bounds__(256, RB == 2 ? 1 : 2) void fla_decode_shared_bf16(c
           s[kb2] = mfma16(__builtin_bit_cast(bf16x8, kreg[kb2][ks]), qf[ks], s[kb2]);
       }
       load_k(jt + 1);
-      const int lim = ke - 1 - k0 - grp * 4;
+      const int lim = min(ke, my_len) - 1 - k0 - grp * 4;
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll

@@ -185,7 +185,7 @@ Plan make_plan(const AttnShape& s, bool decode, const int32_t* q_len, const int3
   if (s.dtype == LRA_DTYPE_F32) {
     for (size_t i = 0; i < n; ++i) {
       const int ql = decode ? 1 : q_len[p.active[i]];
-      p.n_rt[i] = (int)ceil_div(ql, 64);
+      p.n_rt[i] = (int)ceil_div(ql, 16);   // 16 query rows per fp32 workgroup
     }
     return p;
   }
@@ -263,10 +263,14 @@ int run_attention(const AttnShape& s, bool decode, const Requests& rq, const voi
     a.agents[i].rank = ad.ranks[i];
   }
   const size_t n = p.active.size();
-  // Units: requests that one work item serves together.  Decode requests that read the same
-  // base rows (equal k_start and k_len) share every K/V tile, so they are grouped, up to
-  // kMaxMembers (and 16 / G query columns) per unit, members consecutive in launch order;
-  // every other request is a unit of its own.
+  // Units: requests that one work item serves together.  Decode requests whose base rows
+  // start at the same row share every K/V tile of the shorter one's rows (one context read
+  // by several agents, some of which have seen more of it), so they are grouped, up to
+  // kMaxMembers (and 16 / G query columns) per unit, members consecutive in launch order and
+  // longest first: the unit streams the first member's rows once, and each member's query
+  // columns are masked past its own length.  Members also share their key-split count when
+  // planned alone, so the unit's splits fit every member's share of the workspace.  Every
+  // other request is a unit of its own.
   std::vector<int> unit_size(n, 1);
   if (decode && s.dtype == LRA_DTYPE_BF16 && !expand && group_decode_enabled()) {
     const int cap = std::min(lra::kMaxMembers, 16 / G);
@@ -282,7 +286,7 @@ int run_attention(const AttnShape& s, bool decode, const Requests& rq, const voi
       std::vector<std::pair<int32_t, int32_t>> first_seen;
       for (size_t i = 0; i < n; ++i) {
         const int b = p.active[i];
-        const auto key = std::make_pair(rq.k_start[b], rq.k_len[b]);
+        const auto key = std::make_pair(rq.k_start[b], p.n_split[i]);
         auto it = groups.find(key);
         if (it == groups.end()) {
           first_seen.push_back(key);
@@ -291,6 +295,10 @@ int run_attention(const AttnShape& s, bool decode, const Requests& rq, const voi
           it->second.push_back(i);
         }
       }
+      for (auto& kv : groups)   // longest first (stable: equal lengths keep batch order)
+        std::stable_sort(kv.second.begin(), kv.second.end(), [&](size_t x, size_t y) {
+          return rq.k_len[p.active[x]] > rq.k_len[p.active[y]];
+        });
       std::vector<size_t> order;
       unit_size.clear();
       for (const auto& key : first_seen) {

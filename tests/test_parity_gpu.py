@@ -224,6 +224,29 @@ def test_bf16_decode_shared_contexts(shape, chunk, monkeypatch):
     assert (grouped.float() - single.float()).abs().max().item() <= 4e-3
 
 
+@pytest.mark.parametrize("chunk", ["1024", "100000"])
+def test_bf16_decode_shared_context_unequal_lengths(chunk, monkeypatch):
+    """Agents that have seen different lengths of one context: same first row, different
+    k_len.  Requests with equal solo split counts form one unit that streams the longest
+    member's rows once; every member's columns are masked past its own length."""
+    monkeypatch.setenv("LRA_DECODE_CHUNK", chunk)
+    k_len = [3000, 2500, 2049, 1025, 3000, 700, 1]
+    agents = [0, 1, 2, 3, 1, 2, 0]
+    n = len(k_len)
+    prob = workloads.AttnProblem(
+        name="bf16-decode-nested", dtype="bf16", n_q_heads=32, n_kv_heads=8, head_dim=128,
+        ranks=(16, 64, 8, 0), q_start=np.arange(n, dtype=np.int32), q_len=np.ones(n, np.int32),
+        k_start=np.full(n, 100, np.int32), k_len=np.asarray(k_len, np.int32),
+        agent_idx=np.asarray(agents, np.int32), q_rows=n, kv_rows=3100, seed=697)
+    cpu, dev = H.device_inputs(prob)
+    grouped = H.run_decode(prob, dev)
+    _cmp_full(prob, cpu, grouped, what="nested contexts")
+    assert torch.equal(grouped, H.run_decode(prob, dev)), "repeat call not bitwise identical"
+    monkeypatch.setenv("LRA_DECODE_GROUP", "0")
+    single = H.run_decode(prob, dev)
+    assert (grouped.float() - single.float()).abs().max().item() <= 4e-3
+
+
 def test_bf16_decode_shared_lr_cache():
     # BaseLRShared: every agent's LR cache is one buffer; the B_a still differ
     prob = workloads.shared_decode("bf16-decode-lrshared", 32, 8, 128, (16, 16, 16),
