@@ -7,8 +7,8 @@
 // rounded to bf16.  It exists to measure the regrouping against (a full-width V_full
 // followed by plain attention with no adapter), not as part of the regrouped path.
 //
-// A workgroup (4 waves) owns one kv head and up to kExpandRows rows of one span, in tiles
-// of 32 rows.  The product is an MFMA contraction over the rank: wave w computes the
+// A workgroup (4 waves) owns one kv head and up to rows_per_item rows (at most 512) of one
+// span, in tiles of 32 rows.  The product is an MFMA contraction over the rank: wave w computes the
 // transposed block (L·B_g)ᵀ[32w .. 32w+31, rows] = B_gᵀ·Lᵀ with v_mfma_f32_32x32x16_bf16,
 // its B_gᵀ fragments held in registers for the whole work item and the L rows loaded
 // straight into the other operand.  The fp32 block goes through LDS so that the V_base
@@ -51,8 +51,8 @@ __global__ __launch_bounds__(256) void lr_expand_bf16(const ExpandArgs args) {
   const int Hkv = A->Hkv;
   const int local = w - S.work_start;
   const int g = local % Hkv;
-  const int64_t r_begin = S.start + (int64_t)(local / Hkv) * kExpandRows;
-  const int64_t r_end = min(S.start + (int64_t)S.len, r_begin + kExpandRows);
+  const int64_t r_begin = S.start + (int64_t)(local / Hkv) * A->rows_per_item;
+  const int64_t r_end = min(S.start + (int64_t)S.len, r_begin + A->rows_per_item);
   const AgentDesc& AG = A->agents[S.agent];
   const int rank = AG.rank;
   const int64_t kv_stride = (int64_t)Hkv * D;

@@ -673,6 +673,12 @@ int lra_expand_values(int dtype, int32_t n_spans, const int32_t* start, const in
     a.agents[i].ldl = ldl[i];
     a.agents[i].rank = ranks[i];
   }
+  // rows per work item: enough items to cover the CUs several times over (at least 2048
+  // when the rows allow it), at most kExpandRows, in whole 32-row tiles
+  int64_t total_rows = 0;
+  for (int i = 0; i < n_spans; ++i) total_rows += len[i];
+  const int64_t want = ceil_div(total_rows * n_kv_heads, 2048);
+  a.rows_per_item = (int)std::min<int64_t>(lra::kExpandRows, std::max<int64_t>(32, ceil_div(want, 32) * 32));
   int i0 = 0;
   while (i0 < n_spans) {
     int64_t work = 0;
@@ -684,7 +690,7 @@ int lra_expand_values(int dtype, int32_t n_spans, const int32_t* start, const in
       sp.len = len[i0];
       sp.agent = agent_idx[i0];
       sp.work_start = (int)work;
-      work += ceil_div(len[i0], lra::kExpandRows) * n_kv_heads;
+      work += ceil_div(len[i0], a.rows_per_item) * n_kv_heads;
       max_rank = std::max(max_rank, ranks[agent_idx[i0]]);
     }
     if (n == 0) break;

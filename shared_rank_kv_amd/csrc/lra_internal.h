@@ -99,7 +99,8 @@ struct AppendArgs {
 
 // Naive value expansion (the comparator of the regrouped kernels): span i covers rows
 // [start, start + len) of V_base, expanded with agent `agent`'s L and B into the same rows
-// of V_full.  Work items: (chunk of kExpandRows rows, kv head) with the kv head fastest.
+// of V_full.  Work items: (chunk of rows_per_item rows, kv head) with the kv head fastest;
+// rows_per_item is a multiple of 32 up to kExpandRows.
 constexpr int kExpandRows = 512;
 struct ExpandSpan {
   int64_t start;
@@ -108,7 +109,7 @@ struct ExpandSpan {
 struct ExpandArgs {
   const void* V;
   void* Vout;
-  int32_t Hkv, n_span, n_work, pad_;
+  int32_t Hkv, n_span, n_work, rows_per_item;
   AgentDesc agents[kMaxAgents];
   ExpandSpan spans[kReqsPerLaunch];
 };

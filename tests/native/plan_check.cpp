@@ -276,7 +276,8 @@ static void check_comparators() {
     for (int i = 0; i < a.n_span; ++i) {
       const lra::ExpandSpan& sp = a.spans[i];
       assert(sp.len > 0 && sp.work_start == work);
-      work += (int64_t)((sp.len + lra::kExpandRows - 1) / lra::kExpandRows) * 8;
+      assert(a.rows_per_item % 32 == 0 && a.rows_per_item >= 32 && a.rows_per_item <= lra::kExpandRows);
+      work += (int64_t)((sp.len + a.rows_per_item - 1) / a.rows_per_item) * 8;
       ++seen;
     }
     assert(work == a.n_work && a.n_span <= lra::kReqsPerLaunch);
