@@ -90,32 +90,35 @@ constexpr int kOutOfRange = 0x7ffffff0;   // a byte offset past every record cou
 
 // Direct buffer->LDS loads of 64-key tiles.  A tile's buffer resource starts at its first
 // key row and covers only the rows inside the key range, so rows past the range (and LR
-// columns past the rank, addressed out of range) land in LDS as zeros; the per-lane byte
-// offsets below are fixed for the whole key loop and each wave writes the 1 KB LDS units
-// u = wave, wave+4, ...  K/V rows are D*2 bytes; LDS slot p of a row holds source chunk
-// p ^ swz(row).  The LR tile is 64 x 64 bf16 (128-byte rows) whose 64-byte halves are
-// swapped on rows with bit 1 set.
+// columns past the rank, addressed out of range) land in LDS as zeros.  Each wave writes
+// the 1 KB LDS units u = wave, wave+4, ...; unit i of a wave lies NW*RPU rows (K/V) or 32
+// rows (L) below its unit 0 with the same swizzle, so one per-lane byte offset, fixed for
+// the whole key loop, plus a uniform stride addresses them all.  K/V rows are D*2 bytes;
+// LDS slot p of a row holds source chunk p ^ swz(row), with swz_k for K and swz_v for V_base
+// and B_g (the loader of a wave takes the one its tiles need).  The LR tile is 64 x 64 bf16
+// (128-byte rows) whose 64-byte halves are swapped on rows with bit 1 set.
 template <int D, int NW = 4>
 struct TileLoader {
   static constexpr int CPR = D / 8;          // 16-byte chunks per K/V row
   static constexpr int RPU = 64 / CPR;       // rows per 1 KB unit
   static constexpr int UPW = 64 / RPU / NW;  // K (and V) units per wave
   static constexpr int LPW = 8 / NW;         // LR units per wave
-  int koff[UPW], voff[UPW], loff[LPW];
-  __device__ __forceinline__ TileLoader(int wave, int lane, int row_bytes, int l_row_bytes,
-                                        int rank) {
-#pragma unroll
-    for (int i = 0; i < UPW; ++i) {
-      const int row = (wave + NW * i) * RPU + lane / CPR;
-      koff[i] = row * row_bytes + (((lane % CPR) ^ swz_k<D>(row)) << 4);
-      voff[i] = row * row_bytes + (((lane % CPR) ^ swz_v<D>(row)) << 4);
-    }
-#pragma unroll
-    for (int i = 0; i < LPW; ++i) {
-      const int row = (wave + NW * i) * 8 + (lane >> 3);
-      const int c = (lane & 7) ^ (((row >> 1) & 1) * 4);
-      loff[i] = c * 8 < rank ? row * l_row_bytes + c * 16 : kOutOfRange;
-    }
+  int uoff, loff;                            // unit 0 of the wave (K or V layout; L)
+  __device__ __forceinline__ TileLoader(int wave, int lane, bool v_layout, int row_bytes,
+                                        int l_row_bytes, int rank) {
+    const int row = wave * RPU + lane / CPR;
+    const int swz = v_layout ? swz_v<D>(row) : swz_k<D>(row);
+    uoff = row * row_bytes + (((lane % CPR) ^ swz) << 4);
+    const int lrow = wave * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ (((lrow >> 1) & 1) * 4);
+    loff = c * 8 < rank ? lrow * l_row_bytes + c * 16 : kOutOfRange;
+  }
+  // byte offsets of unit i (unsigned wrap keeps an out-of-range L offset out of range)
+  __device__ __forceinline__ int unit(int i, int row_bytes) const {
+    return uoff + i * (NW * RPU) * row_bytes;
+  }
+  __device__ __forceinline__ int lunit(int i, int l_row_bytes) const {
+    return (int)((unsigned)loff + (unsigned)(i * NW * 8 * l_row_bytes));
   }
 };
 
@@ -300,7 +303,7 @@ __global__ __launch_bounds__(512, 1) void fla_prefill_bf16(const AttnArgs args) 
   const int row_bytes = (int)(kv_stride * 2), l_row_bytes = (int)(ldl * 2);
   // tile loads are split by part: group A (waves 0-3) loads K, group B (waves 4-7) loads
   // V_base and L, each during its own softmax phase (see step below)
-  const TileLoader<D, 4> ld(wave & 3, lane, row_bytes, l_row_bytes, rank);
+  const TileLoader<D, 4> ld(wave & 3, lane, group_b, row_bytes, l_row_bytes, rank);
   constexpr int N_K = TileLoader<D, 4>::UPW;                       // K loads per A wave
   constexpr int N_V = TileLoader<D, 4>::UPW + (RB ? TileLoader<D, 4>::LPW : 0);   // per B wave
   auto tile_rows = [&](int k0) {
@@ -309,20 +312,20 @@ __global__ __launch_bounds__(512, 1) void fla_prefill_bf16(const AttnArgs args) 
   auto load_k = [&](int k0, LDS char* dst) {   // this A wave's units of K rows k0..k0+63
     const auto kr = rows_rsrc(Kg + (int64_t)k0 * kv_stride, tile_rows(k0) * row_bytes);
 #pragma unroll
-    for (int i = 0; i < N_K; ++i) load_unit(kr, dst + ((wave & 3) + 4 * i) * 1024, ld.koff[i]);
+    for (int i = 0; i < N_K; ++i) load_unit(kr, dst + ((wave & 3) + 4 * i) * 1024, ld.unit(i, row_bytes));
   };
   auto load_vl = [&](int k0, LDS char* dst) {  // this B wave's units of V_base and L rows
     const int rows = tile_rows(k0);
     const auto vr = rows_rsrc(Vg + (int64_t)k0 * kv_stride, rows * row_bytes);
 #pragma unroll
     for (int i = 0; i < TileLoader<D, 4>::UPW; ++i)
-      load_unit(vr, dst + TILE_KV + ((wave & 3) + 4 * i) * 1024, ld.voff[i]);
+      load_unit(vr, dst + TILE_KV + ((wave & 3) + 4 * i) * 1024, ld.unit(i, row_bytes));
     if (RB) {
       const auto lr = rows_rsrc(rank > 0 ? (const void*)(Lg + (int64_t)k0 * ldl) : (const void*)Kg,
                                 rank > 0 ? rows * l_row_bytes : 0);
 #pragma unroll
       for (int i = 0; i < TileLoader<D, 4>::LPW; ++i)
-        load_unit(lr, dst + 2 * TILE_KV + ((wave & 3) + 4 * i) * 1024, ld.loff[i]);
+        load_unit(lr, dst + 2 * TILE_KV + ((wave & 3) + 4 * i) * 1024, ld.lunit(i, l_row_bytes));
     }
   };
 
@@ -389,12 +392,18 @@ __global__ __launch_bounds__(512, 1) void fla_prefill_bf16(const AttnArgs args) 
     if (!wave_active || j >= n_tiles) return;
     const int k0 = kb + j * kTileKeys;
     if (k0 + kTileKeys > mask_from) {
+      // causal mask as an additive penalty, -inf where the key lies past the row's last
+      // visible key (the sign of lim - key), else +0: pure vector arithmetic.  Written as
+      // compares, the 32 lane masks are kept in scalar register pairs and push the kernel's
+      // loop-carried scalars into VGPR-lane spills that every phase reloads.
       const int lim = vis_last - k0;
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          if (kb2 * 32 + (e >> 2) * 8 + (e & 3) > lim) s[kb2][e] = -INFINITY;
+        for (int e = 0; e < 16; ++e) {
+          const int d = lim - (kb2 * 32 + (e >> 2) * 8 + (e & 3));
+          s[kb2][e] += __builtin_bit_cast(float, (d >> 31) & (int)0xff800000u);
+        }
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -500,7 +509,7 @@ __global__ __launch_bounds__(512, 1) void fla_prefill_bf16(const AttnArgs args) 
       const auto br = rows_rsrc((const bf16*)AG.B + g * D, rank * row_bytes);
 #pragma unroll
       for (int i = 0; i < TileLoader<D, 4>::UPW; ++i)
-        load_unit(br, btile + ((wave & 3) + 4 * i) * 1024, ld.voff[i]);
+        load_unit(br, btile + ((wave & 3) + 4 * i) * 1024, ld.unit(i, row_bytes));
     }
     wait_loads();
   }
@@ -531,7 +540,7 @@ __global__ __launch_bounds__(512, 1) void fla_prefill_bf16(const AttnArgs args) 
       const auto br = rows_rsrc((const bf16*)AG.B + g * D, rank * row_bytes);
 #pragma unroll
       for (int i = 0; i < TileLoader<D, 4>::UPW; ++i)
-        load_unit(br, buf0 + TILE_KV + ((wave & 3) + 4 * i) * 1024, ld.voff[i]);
+        load_unit(br, buf0 + TILE_KV + ((wave & 3) + 4 * i) * 1024, ld.unit(i, row_bytes));
       wait_loads();
     }
     lds_barrier();
