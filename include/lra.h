@@ -55,7 +55,7 @@ enum lra_status {
   LRA_OK = 0,
   LRA_ERR_INVALID = 1,      /* malformed arguments (null pointer, bad shape or range)       */
   LRA_ERR_UNSUPPORTED = 2,  /* well-formed but not implemented (see limits below)           */
-  LRA_ERR_WORKSPACE = 3,    /* workspace pointer null or smaller than lra_attn_workspace_bytes */
+  LRA_ERR_WORKSPACE = 3,    /* workspace pointer null or smaller than the call needs        */
   LRA_ERR_HIP = 4           /* the HIP runtime reported an error while queueing work        */
 };
 
@@ -108,10 +108,15 @@ int lra_precompute_lr(int dtype, int64_t T, int64_t d_model,
  *   L_out    host [n_agents] array of device pointers; L_out[a] is [l_rows, r_a] with row
  *            stride ldl[a]
  *   rows     host [batch]: the cache row of token b, distinct, in [0, l_rows)
+ *   workspace  device scratch of at least lra_append_workspace_bytes(...) bytes, 16-byte
+ *            aligned (may be NULL when that size is 0; it is 0 for fp32): the bf16 path
+ *            splits d_model across workgroups and adds their fp32 partial sums there in a
+ *            fixed order, so results are deterministic.  Its contents on entry do not
+ *            matter; calls that may overlap in time need separate workspaces.
  * Only the rows listed are written.  Same requirements as lra_precompute_lr, and batch <=
- * LRA_MAX_BATCH; duplicate or out-of-range rows are LRA_ERR_INVALID.  The base K/V rows of
- * the new tokens come from the model's own projections and are appended by the caller.
- * batch == 0 is a no-op.
+ * LRA_MAX_BATCH; duplicate or out-of-range rows are LRA_ERR_INVALID, a missing or short
+ * workspace LRA_ERR_WORKSPACE.  The base K/V rows of the new tokens come from the model's
+ * own projections and are appended by the caller.  batch == 0 is a no-op.
  */
 int lra_append_lr(int dtype, int32_t batch, int64_t d_model,
                   const void* X, int64_t ldx,
@@ -119,7 +124,16 @@ int lra_append_lr(int dtype, int32_t batch, int64_t d_model,
                   int32_t n_agents, const int32_t* ranks,
                   void* const* L_out, const int64_t* ldl,
                   const int32_t* rows, int64_t l_rows,
+                  void* workspace, size_t workspace_bytes,
                   void* stream);
+
+/*
+ * lra_append_workspace_bytes -- scratch bytes lra_append_lr needs with these arguments
+ * (ranks: host [n_agents]).  Returns 0 when no scratch is needed (fp32, batch 0, all ranks
+ * 0), and (size_t)-1 when the arguments are invalid.
+ */
+size_t lra_append_workspace_bytes(int dtype, int32_t batch, int64_t d_model,
+                                  int32_t n_agents, const int32_t* ranks);
 
 /*
  * lra_attn_prefill -- Flash-LoRA-Attention over a batch of requests (LRAgent summary,

@@ -556,7 +556,39 @@ int attn_decode_impl(bool expand, int dtype, int32_t batch, int32_t n_q_heads,
 
 namespace lra {
 int report_error(int code, const char* msg) { return fail(code, "%s", msg); }
+
+// One bf16 append launch: 64 x 64 output blocks, and d_model cut into slices of whole
+// 256-value rounds so that the launch has about kAppendItems workgroups (a slice is never
+// shorter than one round).  Every X and A_cat element is read by exactly one workgroup
+// when the tokens fit one block and the columns one block (64 tokens, 64 columns).
+constexpr int kAppendItems = kAppendMaxSlices;   // so that a launch has at most that many slices
+AppendPlan plan_append(int64_t T, int64_t d_model, int64_t R) {
+  AppendPlan p;
+  const int tbn = (int)ceil_div(T, 64), cbn = (int)ceil_div(R, 64);
+  const int nk = (int)(d_model / 32);
+  const int rounds = (int)ceil_div(nk, 8);
+  const int want = std::max(1, kAppendItems / (tbn * cbn));
+  const int per = (int)ceil_div(rounds, std::min(want, rounds));   // rounds per slice
+  p.slice_chunks = per * 8;
+  p.n_slices = (int)ceil_div(nk, p.slice_chunks);
+  p.t_pad = tbn * 64;
+  p.r_pad = cbn * 64;
+  return p;
+}
 }  // namespace lra
+
+namespace {
+// Workspace of an append call: the largest of its launches' partial buffers (the launches
+// run one after another on the call's stream and reuse it).
+size_t append_workspace(int32_t batch, int64_t d_model, int64_t R) {
+  int64_t most = 0;
+  for (int b0 = 0; b0 < batch; b0 += lra::kAppendRows) {
+    const int n = std::min(batch - b0, lra::kAppendRows);
+    most = std::max(most, lra::plan_append(n, d_model, R).bytes());
+  }
+  return (size_t)most;
+}
+}  // namespace
 
 extern "C" {
 
@@ -721,7 +753,7 @@ int lra_precompute_lr(int dtype, int64_t T, int64_t d_model, const void* X, int6
 int lra_append_lr(int dtype, int32_t batch, int64_t d_model, const void* X, int64_t ldx,
                   const void* A_cat, int64_t lda, int32_t n_agents, const int32_t* ranks,
                   void* const* L_out, const int64_t* ldl, const int32_t* rows, int64_t l_rows,
-                  void* stream) {
+                  void* workspace, size_t workspace_bytes, void* stream) {
   if (batch < 0) return fail(LRA_ERR_INVALID, "batch %d < 0", batch);
   if (batch > LRA_MAX_BATCH)
     return fail(LRA_ERR_UNSUPPORTED, "batch %d > LRA_MAX_BATCH (%d)", batch, LRA_MAX_BATCH);
@@ -742,18 +774,49 @@ int lra_append_lr(int dtype, int32_t batch, int64_t d_model, const void* X, int6
       return fail(LRA_ERR_INVALID, "rows: row %d appears twice", sorted[b]);
   }
   if (R == 0) return ok();
+  const bool bf16 = dtype == LRA_DTYPE_BF16;
+  const size_t need = bf16 ? append_workspace(batch, d_model, R) : 0;
+  if (need > 0 && !workspace)
+    return fail(LRA_ERR_WORKSPACE, "workspace is null; %zu bytes needed", need);
+  if (workspace_bytes < need)
+    return fail(LRA_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes, need);
+  if (need > 0 && !aligned(workspace, 16))
+    return fail(LRA_ERR_INVALID, "workspace must be 16-byte aligned");
   const char* Xb = static_cast<const char*>(X);
-  const int64_t esz = dtype == LRA_DTYPE_BF16 ? 2 : 4;
+  const int64_t esz = bf16 ? 2 : 4;
   for (int b0 = 0; b0 < batch; b0 += lra::kAppendRows) {
     const int n = std::min(batch - b0, lra::kAppendRows);
     a.p.X = Xb + (int64_t)b0 * ldx * esz;
     a.p.T = n;
     for (int i = 0; i < n; ++i) a.rows[i] = rows[b0 + i];
-    hipError_t e = dtype == LRA_DTYPE_BF16 ? lra::launch_append_bf16(a, (hipStream_t)stream)
-                                           : lra::launch_append_f32(a, (hipStream_t)stream);
+    if (bf16) {
+      const lra::AppendPlan pl = lra::plan_append(n, d_model, R);
+      a.part = static_cast<float*>(workspace);
+      a.n_slices = pl.n_slices;
+      a.slice_chunks = pl.slice_chunks;
+      a.t_pad = pl.t_pad;
+      a.r_pad = pl.r_pad;
+    }
+    hipError_t e = bf16 ? lra::launch_append_bf16(a, (hipStream_t)stream)
+                        : lra::launch_append_f32(a, (hipStream_t)stream);
     if (e != hipSuccess) return fail(LRA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   }
   return ok();
+}
+
+size_t lra_append_workspace_bytes(int dtype, int32_t batch, int64_t d_model, int32_t n_agents,
+                                  const int32_t* ranks) {
+  if ((dtype != LRA_DTYPE_F32 && dtype != LRA_DTYPE_BF16) || batch < 0 ||
+      batch > LRA_MAX_BATCH || d_model <= 0 || n_agents <= 0 || n_agents > LRA_MAX_AGENTS ||
+      !ranks)
+    return (size_t)-1;
+  int64_t R = 0;
+  for (int i = 0; i < n_agents; ++i) {
+    if (ranks[i] < 0) return (size_t)-1;
+    R += ranks[i];
+  }
+  if (dtype != LRA_DTYPE_BF16 || batch == 0 || R == 0) return 0;
+  return append_workspace(batch, d_model, R);
 }
 
 }  // extern "C"

@@ -90,12 +90,23 @@ struct PrecomputeArgs {
 };
 
 // Decode-step append: the LR rows of up to kAppendRows new tokens per launch.  Token t of
-// the launch goes to row rows[t] of every agent's cache.
+// the launch goes to row rows[t] of every agent's cache.  bf16: d_model is cut into
+// n_slices slices of slice_chunks 32-value chunks; slice s leaves its fp32 partial sums in
+// part[s][t][c] ([n_slices][t_pad][r_pad] in the workspace, t_pad and r_pad multiples of 64).
 constexpr int kAppendRows = 256;
+constexpr int kAppendMaxSlices = 16;
 struct AppendArgs {
   PrecomputeArgs p;    // X holds the launch's tokens (T of them), A_cat, the agents' caches
+  float* part;
+  int32_t n_slices, slice_chunks, t_pad, r_pad;
   int32_t rows[kAppendRows];
 };
+// The split of one bf16 append launch of T tokens (T <= kAppendRows) and R columns.
+struct AppendPlan {
+  int32_t n_slices, slice_chunks, t_pad, r_pad;
+  int64_t bytes() const { return (int64_t)n_slices * t_pad * r_pad * 4; }
+};
+AppendPlan plan_append(int64_t T, int64_t d_model, int64_t R);
 
 // Naive value expansion (the comparator of the regrouped kernels): span i covers rows
 // [start, start + len) of V_base, expanded with agent `agent`'s L and B into the same rows

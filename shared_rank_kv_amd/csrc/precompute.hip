@@ -316,90 +316,142 @@ __global__ __launch_bounds__(256) void lr_precompute_f32(const PrecomputeArgs ar
 // ---------------------------------------------------------------------------------------
 // Decode-step append: the LR rows of a few new tokens, L_a[rows[t]] = x_t·A_a for every
 // agent (the LR caches of PreLRShared kept current as tokens are generated).  The product
-// is tiny in tokens and long in d_model, so a workgroup owns 16 tokens x 16 columns and its
-// sixteen waves split d_model (32-value chunks dealt round-robin); the waves' sums meet in
-// LDS and are added in a fixed order, so results are deterministic and need no workspace.
-// The operands are those of the precompute: the X rows are the B operand (straight from
-// memory), each [32 x 16] A_cat block passes through LDS, rows permuted (a_k) for the
-// transposing read.  A wave issues the loads of a round of eight chunks together, waits
-// once, stores the round's eight blocks and then runs its MFMAs on four accumulators, so a
-// round costs one memory latency (d_model 4096 is one round).
-constexpr int kAppendWaves = 16;
-constexpr int kAppendRound = 8;               // chunks per wave per round
+// is tiny in tokens and long in d_model, and at this size it is bound by memory latency, so
+// d_model is split across workgroups and every X and A_cat element is read by exactly one
+// of them (no workgroup re-reads another's data), in two passes over a caller workspace:
+//
+// pass 1 (lr_append_part_bf16): workgroup (slice s, token block tb, column block cb) with
+//   64 tokens x 64 columns and the d_model values of slice s, in rounds of 256 values (eight
+//   32-value chunks).  Wave (ts, kq) takes token sub-block ts (16 tokens), all 64 columns,
+//   and chunks kq and kq + 4 of each round.  As in the precompute the product is computed
+//   transposed with v_mfma_f32_16x16x32_bf16: the X rows are the B operand (straight from
+//   memory); the [32 x 16] A_cat blocks of a round (chunk x column sub-block) pass through
+//   LDS, rows permuted (a_k) for the transposing read, each loaded by one wave for the
+//   four that use it.  The next round's loads are in flight during a round's MFMAs.  The
+//   four k-quarters of a token sub-block meet in LDS and are added in a fixed order into the
+//   slice's fp32 partial part[s][t][c].
+// pass 2 (lr_append_sum_bf16): one thread per (token, column) adds the slices' partials in
+//   slice order, rounds to bf16 and writes the token's cache row.
+// Both passes add in a fixed order, so results are deterministic.
+constexpr int kAppendRoundChunks = 8;         // 32-value chunks per round
 
-__global__ __launch_bounds__(64 * kAppendWaves) void lr_append_bf16(const AppendArgs args) {
+__global__ __launch_bounds__(1024) void lr_append_part_bf16(const AppendArgs args) {
   const AppendArgs* AA = (const AppendArgs*)__builtin_amdgcn_kernarg_segment_ptr();
   const PrecomputeArgs* P = &AA->p;
-  __shared__ __attribute__((aligned(16))) char tiles[kAppendWaves][kAppendRound][1024];
-  __shared__ float part[kAppendWaves][16][17];
+  __shared__ __attribute__((aligned(16))) char tiles[4 * kAppendRoundChunks][1024];
+  __shared__ float red[4][64][65];              // [k-quarter][token][column]
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ts = wave & 3, kq = wave >> 2;
   const int grp = lane >> 4, col = lane & 15;
-  const int cb = blockIdx.x, tb = blockIdx.y;
+  const int s = blockIdx.x, tb = blockIdx.y, cb = blockIdx.z;
   const int64_t T = P->T, ldx = P->ldx, lda = P->lda;
   const int R = P->R;
   const int nk = (int)(P->d_model / 32);
+  const int k_lo = s * AA->slice_chunks;                   // this slice's chunks
+  const int k_hi = min(nk, k_lo + AA->slice_chunks);
+  const int n_rounds = (k_hi - k_lo + kAppendRoundChunks - 1) / kAppendRoundChunks;
 
-  // X: lane (grp, col) holds token 16 tb + col, d_model values 32 j + 8 grp .. + 8
-  const int64_t t0 = (int64_t)tb * 16;
+  // X: lane (grp, col) holds token 64 tb + 16 ts + col, d_model values 32 j + 8 grp .. + 8
+  const int64_t t0 = (int64_t)tb * 64 + ts * 16;
   const int64_t left = T - t0;
   const int x_rows = left <= 0 ? 0 : (left < 16 ? (int)left : 16);
-  const __amdgpu_buffer_rsrc_t xr = make_rsrc((const char*)P->X + t0 * ldx * 2,
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc((const char*)P->X + (x_rows ? t0 * ldx * 2 : 0),
                                               (int)(x_rows * ldx * 2));
   const int xoff = (int)(col * ldx * 2) + grp * 16;
-  // A_cat block of chunk j: lane l loads 8 columns (16 cb + 8 (l & 1) ..) of A_cat row
-  // 32 j + a_k(l / 2), which the LDS block keeps at row l / 2: offset 16 l
-  const int c8 = cb * 16 + 8 * (lane & 1);
+  // A blocks: this wave loads blocks b = wave and wave + 16 of each round (chunk b / 4,
+  // column sub-block b % 4); lane l loads 8 columns (64 cb + 16 (b % 4) + 8 (l & 1) ..) of
+  // A_cat row 32 j + a_k(l / 2), which the LDS block keeps at row l / 2: offset 16 l
   const __amdgpu_buffer_rsrc_t ar = make_rsrc(P->A, (int)(P->d_model * lda * 2));
-  const int aoff = c8 < R ? (int)((a_k(lane >> 1) * lda + c8) * 2) : kOutOfRange;
+  int aoff[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c8 = cb * 64 + 16 * ((wave + 16 * i) & 3) + 8 * (lane & 1);
+    aoff[i] = c8 < R ? (int)((a_k(lane >> 1) * lda + c8) * 2) : kOutOfRange;
+  }
   const int a_chunk = (int)(32 * lda * 2);      // bytes of 32 A_cat rows
   // transposing read: lane (grp, e, q) points at block row 4 grp + e (then + 16), columns
   // 4 q .. + 4, and receives column col, d_model values 8 grp .. + 8 of the chunk
   const int toff = (4 * grp + (col >> 2)) * 32 + (col & 3) * 8;
 
-  const int my = nk > wave ? (nk - wave + kAppendWaves - 1) / kAppendWaves : 0;
+  // chunks past the slice read zeros (soffset past every record)
+  auto x_soff = [&](int r, int i) {
+    const int j = k_lo + r * kAppendRoundChunks + kq + 4 * i;
+    return __builtin_amdgcn_readfirstlane(r < n_rounds && j < k_hi ? j * 64 : kOutOfRange);
+  };
+  auto a_soff = [&](int r, int i) {
+    const int j = k_lo + r * kAppendRoundChunks + ((wave + 16 * i) >> 2);
+    return __builtin_amdgcn_readfirstlane(r < n_rounds && j < k_hi ? j * a_chunk : kOutOfRange);
+  };
+  u32x4 xq[2], aq[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    xq[i] = load_b128(xr, xoff, x_soff(0, i));
+    aq[i] = load_b128(ar, aoff[i], a_soff(0, i));
+  }
   f32x4 acc[4] = {f32x4{}, f32x4{}, f32x4{}, f32x4{}};
-  for (int r0 = 0; r0 < my; r0 += kAppendRound) {
-    u32x4 xq[kAppendRound], aq[kAppendRound];
+  for (int r = 0; r < n_rounds; ++r) {
 #pragma unroll
-    for (int i = 0; i < kAppendRound; ++i) {
-      // chunks past this wave's last read zeros (soffset past every record)
-      const int j = wave + (r0 + i) * kAppendWaves;
-      const bool ok = r0 + i < my;
-      xq[i] = load_b128(xr, xoff, __builtin_amdgcn_readfirstlane(ok ? j * 64 : kOutOfRange));
-      aq[i] = load_b128(ar, aoff, __builtin_amdgcn_readfirstlane(ok ? j * a_chunk : kOutOfRange));
+    for (int i = 0; i < 2; ++i)
+      *(LDS u32x4*)((LDS char*)tiles[wave + 16 * i] + lane * 16) = aq[i];
+    const u32x4 x0 = xq[0], x1 = xq[1];
+    if (r + 1 < n_rounds) {                    // the next round's loads, during this one
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        xq[i] = load_b128(xr, xoff, x_soff(r + 1, i));
+        aq[i] = load_b128(ar, aoff[i], a_soff(r + 1, i));
+      }
     }
-    // the previous round's reads of these blocks precede the writes in program order, and
-    // the LDS executes one wave's operations in order
+    lds_barrier();
 #pragma unroll
-    for (int i = 0; i < kAppendRound; ++i)
-      *(LDS u32x4*)((LDS char*)tiles[wave][i] + lane * 16) = aq[i];
-#pragma unroll
-    for (int i = 0; i < kAppendRound; ++i) {
-      const LDS char* t = (const LDS char*)tiles[wave][i];
-      const bf16x8 aop = join(tr_read(t + toff), tr_read(t + toff + 16 * 32));
-      acc[i & 3] = mfma16(aop, __builtin_bit_cast(bf16x8, xq[i]), acc[i & 3]);
+    for (int cs = 0; cs < 4; ++cs) {
+      const LDS char* t0b = (const LDS char*)tiles[4 * kq + cs];
+      const LDS char* t1b = (const LDS char*)tiles[4 * (kq + 4) + cs];
+      acc[cs] = mfma16(join(tr_read(t0b + toff), tr_read(t0b + toff + 16 * 32)),
+                       __builtin_bit_cast(bf16x8, x0), acc[cs]);
+      acc[cs] = mfma16(join(tr_read(t1b + toff), tr_read(t1b + toff + 16 * 32)),
+                       __builtin_bit_cast(bf16x8, x1), acc[cs]);
     }
+    lds_barrier();                             // the round's reads before the next stores
   }
-  // acc register j of lane (grp, col): column 16 cb + 4 grp + j, token 16 tb + col
+  // acc[cs] register j of lane (grp, col): column 16 cs + 4 grp + j, token 16 ts + col
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    part[wave][4 * grp + j][col] = (acc[0][j] + acc[1][j]) + (acc[2][j] + acc[3][j]);
+  for (int cs = 0; cs < 4; ++cs)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) red[kq][16 * ts + col][16 * cs + 4 * grp + j] = acc[cs][j];
   __syncthreads();
-  if (tid < 256) {
-    const int cl = tid & 15, tl = tid >> 4;           // column, token of this thread
-    const int c = cb * 16 + cl;
-    const int64_t t = t0 + tl;
-    if (c < R && t < T) {
-      float v = 0.f;
-#pragma unroll
-      for (int w = 0; w < kAppendWaves; ++w) v += part[w][cl][tl];
-      int a = 0;
-      while (a + 1 < P->n_agents && P->col_start[a + 1] <= c) ++a;
-      bf16* Lp = (bf16*)P->Lout[a];
-      Lp[(int64_t)AA->rows[t] * P->ldl[a] + (c - P->col_start[a])] = (bf16)v;
-    }
+  float* part = AA->part + ((int64_t)s * AA->t_pad + tb * 64) * AA->r_pad + cb * 64;
+  for (int e = tid; e < 64 * 64; e += 1024) {
+    const int tl = e >> 6, cl = e & 63;
+    part[(int64_t)tl * AA->r_pad + cl] =
+        ((red[0][tl][cl] + red[1][tl][cl]) + red[2][tl][cl]) + red[3][tl][cl];
   }
+}
+
+// pass 2: thread (token t, columns 4 q .. 4 q + 3); the slices' partials (at most
+// kAppendMaxSlices) are all requested before the first is added.  Ranks are multiples of 8,
+// so the four columns belong to one agent.
+__global__ __launch_bounds__(256) void lr_append_sum_bf16(const AppendArgs args) {
+  const AppendArgs* AA = (const AppendArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+  const PrecomputeArgs* P = &AA->p;
+  const int R4 = P->R / 4;
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= P->T * R4) return;
+  const int t = (int)(e / R4), c = 4 * (int)(e % R4);
+  const f32x4* src = (const f32x4*)(AA->part + (int64_t)t * AA->r_pad + c);
+  const int64_t stride = (int64_t)AA->t_pad * AA->r_pad / 4;
+  const int n = AA->n_slices;
+  f32x4 p[kAppendMaxSlices];
+#pragma unroll
+  for (int s = 0; s < kAppendMaxSlices; ++s) p[s] = s < n ? src[s * stride] : f32x4{};
+  f32x4 v = p[0];
+#pragma unroll
+  for (int s = 1; s < kAppendMaxSlices; ++s) v += p[s];
+  int a = 0;
+  while (a + 1 < P->n_agents && P->col_start[a + 1] <= c) ++a;
+  bf16* Lp = (bf16*)P->Lout[a] + (int64_t)AA->rows[t] * P->ldl[a] + (c - P->col_start[a]);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) Lp[j] = (bf16)v[j];
 }
 
 // fp32 append: one thread per (token, column), a plain fp32 dot product over d_model.
@@ -444,8 +496,12 @@ hipError_t launch_precompute_f32(const PrecomputeArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_append_bf16(const AppendArgs& a, hipStream_t s) {
-  const dim3 grid((a.p.R + 15) / 16, (unsigned)((a.p.T + 15) / 16));
-  hipLaunchKernelGGL(lr_append_bf16, grid, dim3(64 * kAppendWaves), 0, s, a);
+  const dim3 grid((unsigned)a.n_slices, (unsigned)(a.t_pad / 64), (unsigned)(a.r_pad / 64));
+  hipLaunchKernelGGL(lr_append_part_bf16, grid, dim3(1024), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t n = a.p.T * (a.p.R / 4);
+  hipLaunchKernelGGL(lr_append_sum_bf16, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

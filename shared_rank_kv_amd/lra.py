@@ -23,7 +23,8 @@ LRA_DTYPE_F32, LRA_DTYPE_BF16 = 0, 1
 NOALLOC_SCRATCH_BYTES = 32 << 20      # LRA_NOALLOC_SCRATCH_BYTES of include/lra.h
 SYMBOLS = ("lra_precompute_lr", "lra_append_lr", "lra_attn_prefill", "lra_attn_decode",
            "lra_expand_values", "lra_attn_prefill_expand", "lra_attn_decode_expand",
-           "lra_attn_decode_noalloc", "lra_attn_workspace_bytes", "lra_last_error")
+           "lra_attn_decode_noalloc", "lra_attn_workspace_bytes", "lra_append_workspace_bytes",
+           "lra_last_error")
 
 _c_i32p = ctypes.POINTER(ctypes.c_int32)
 _c_i64p = ctypes.POINTER(ctypes.c_int64)
@@ -44,7 +45,7 @@ def _load():
     lib.lra_precompute_lr.argtypes = [ctypes.c_int, L, L, P, L, P, L, I, _c_i32p, _c_vpp, _c_i64p, P]
     lib.lra_precompute_lr.restype = ctypes.c_int
     lib.lra_append_lr.argtypes = [ctypes.c_int, I, L, P, L, P, L, I, _c_i32p, _c_vpp, _c_i64p,
-                                  _c_i32p, L, P]
+                                  _c_i32p, L, P, S, P]
     lib.lra_append_lr.restype = ctypes.c_int
     lib.lra_attn_prefill.argtypes = [ctypes.c_int, I, I, I, I, _c_i32p, _c_i32p, _c_i32p, _c_i32p,
                                      _c_i32p, P, L, P, P, L, I, _c_i32p, _c_vpp, _c_i64p, _c_vpp,
@@ -67,6 +68,8 @@ def _load():
     lib.lra_attn_workspace_bytes.argtypes = [ctypes.c_int, ctypes.c_int, I, _c_i32p, _c_i32p, I, I,
                                              I, I]
     lib.lra_attn_workspace_bytes.restype = ctypes.c_size_t
+    lib.lra_append_workspace_bytes.argtypes = [ctypes.c_int, I, L, I, _c_i32p]
+    lib.lra_append_workspace_bytes.restype = ctypes.c_size_t
     lib.lra_last_error.argtypes = []
     lib.lra_last_error.restype = ctypes.c_char_p
     return lib
@@ -246,12 +249,24 @@ def lra_precompute_lr(X, A_cat, ranks, L_out, stream=None):
     return prepare_precompute_lr(X, A_cat, ranks, L_out)(stream)
 
 
-def prepare_append_lr(X, A_cat, ranks, L_out, rows):
+def lra_append_workspace_bytes(dtype, batch, d_model, ranks):
+    """Scratch bytes of an lra_append_lr call (dtype: torch dtype or LRA_DTYPE_*)."""
+    if isinstance(dtype, torch.dtype):
+        dtype = LRA_DTYPE_BF16 if dtype == torch.bfloat16 else LRA_DTYPE_F32
+    rk, rkp = _i32(ranks)
+    n = lib.lra_append_workspace_bytes(dtype, int(batch), int(d_model), len(rk), rkp)
+    if n == ctypes.c_size_t(-1).value:
+        raise LraError(LRA_ERR_INVALID, "invalid arguments to lra_append_workspace_bytes")
+    return int(n)
+
+
+def prepare_append_lr(X, A_cat, ranks, L_out, rows, workspace=None):
     """Prepared lra_append_lr: L_out[a][rows[b]] <- X[b] · A_cat[:, off_a:off_a + ranks[a]].
 
     X [batch, d_model] (the new tokens), A_cat [d_model, sum(ranks)], L_out: list of
     [l_rows, r_a] GPU tensors sharing l_rows (row stride = stride(0)), rows: batch
-    distinct cache rows.
+    distinct cache rows.  workspace: optional GPU tensor of at least
+    lra_append_workspace_bytes bytes (allocated here when None).
     """
     _dtype(X)
     _lr_outputs(X, A_cat, ranks, L_out)
@@ -260,14 +275,21 @@ def prepare_append_lr(X, A_cat, ranks, L_out, rows):
     ld, ldp = _i64([t.stride(0) if t is not None else 0 for t in L_out])
     rw, rwp = _i32(rows)
     l_rows = max([t.shape[0] for t in L_out if t is not None] + [0])
+    need = lib.lra_append_workspace_bytes(_dtype(X), X.shape[0], X.shape[1], len(rk), rkp)
+    if need == ctypes.c_size_t(-1).value:
+        need = 0      # invalid arguments: the call reports why
+    ws, ws_bytes = _workspace(need, X.device, workspace)
     args = (_dtype(X), X.shape[0], X.shape[1], X.data_ptr(), X.stride(0), A_cat.data_ptr(),
-            A_cat.stride(0), len(rk), rkp, ptrs, ldp, rwp, l_rows, None)
-    return Prepared(lib.lra_append_lr, args, (X, A_cat, L_out, rk, pk, ld, rw), L_out, 13)
+            A_cat.stride(0), len(rk), rkp, ptrs, ldp, rwp, l_rows,
+            ws.data_ptr() if ws is not None else None, ws_bytes, None)
+    return Prepared(lib.lra_append_lr, args, (X, A_cat, L_out, rk, pk, ld, rw, ws), L_out, 15,
+                    owned=(ws if workspace is None else None,))
 
 
-def lra_append_lr(X, A_cat, ranks, L_out, rows, stream=None):
+def lra_append_lr(X, A_cat, ranks, L_out, rows, workspace=None, stream=None):
     """L_out[a][rows[b]] <- X[b] · A_cat[:, off_a:off_a + ranks[a]] (decode-step LR append)."""
-    return prepare_append_lr(X, A_cat, ranks, L_out, rows)(stream)
+    with torch.cuda.stream(stream) if stream is not None else _nullctx():
+        return prepare_append_lr(X, A_cat, ranks, L_out, rows, workspace)(stream)
 
 
 def prepare_attn_prefill(Q, K_base, V_base, L, B, q_start, q_len, k_start, k_len, agent_idx,

@@ -19,6 +19,7 @@
 struct Rec { lra::AttnArgs a; int kind; int grid; bool expand; };   // 0 prefill, 1 decode, 2 decode shared, 3 combine, 4 f32
 static std::vector<Rec> g_recs;
 static std::vector<lra::ExpandArgs> g_expand;
+static std::vector<lra::AppendArgs> g_append;
 namespace lra {
 hipError_t launch_prefill_bf16(const AttnArgs& a, int, int, int grid, hipStream_t, bool ex) { g_recs.push_back({a, 0, grid, ex}); return hipSuccess; }
 hipError_t launch_decode_bf16(const AttnArgs& a, int, int, int, hipStream_t, bool ex) { g_recs.push_back({a, 1, 0, ex}); return hipSuccess; }
@@ -28,7 +29,7 @@ hipError_t launch_combine_bf16(const AttnArgs& a, int, hipStream_t) { g_recs.pus
 hipError_t launch_attn_f32(const AttnArgs& a, int, int, hipStream_t) { g_recs.push_back({a, 4, 0, false}); return hipSuccess; }
 hipError_t launch_precompute_bf16(const PrecomputeArgs&, hipStream_t) { return hipSuccess; }
 hipError_t launch_precompute_f32(const PrecomputeArgs&, hipStream_t) { return hipSuccess; }
-hipError_t launch_append_bf16(const AppendArgs&, hipStream_t) { return hipSuccess; }
+hipError_t launch_append_bf16(const AppendArgs& a, hipStream_t) { g_append.push_back(a); return hipSuccess; }
 hipError_t launch_append_f32(const AppendArgs&, hipStream_t) { return hipSuccess; }
 }
 
@@ -219,18 +220,69 @@ static void check_validation() {
                              big, o5, l5, nullptr), LRA_ERR_UNSUPPORTED, "sum of ranks > 256"); }
   { const int rows[3] = {5, 9, 5};
     expect(lra_append_lr(LRA_DTYPE_BF16, 3, 4096, (void*)0x1000, 4096, (void*)0x2000, 192, 3, ranks,
-                         outs, ldl, rows, 100, nullptr), LRA_ERR_INVALID, "duplicate append rows"); }
+                         outs, ldl, rows, 100, nullptr, 0, nullptr), LRA_ERR_INVALID, "duplicate append rows"); }
   { const int rows[2] = {5, 100};
     expect(lra_append_lr(LRA_DTYPE_BF16, 2, 4096, (void*)0x1000, 4096, (void*)0x2000, 192, 3, ranks,
-                         outs, ldl, rows, 100, nullptr), LRA_ERR_INVALID, "append row out of range"); }
+                         outs, ldl, rows, 100, nullptr, 0, nullptr), LRA_ERR_INVALID, "append row out of range"); }
   { std::vector<int> rows(LRA_MAX_BATCH + 1);
     for (size_t i = 0; i < rows.size(); ++i) rows[i] = (int)i;
     expect(lra_append_lr(LRA_DTYPE_BF16, (int)rows.size(), 4096, (void*)0x1000, 4096, (void*)0x2000,
-                         192, 3, ranks, outs, ldl, rows.data(), 1 << 20, nullptr),
+                         192, 3, ranks, outs, ldl, rows.data(), 1 << 20, nullptr, 0, nullptr),
            LRA_ERR_UNSUPPORTED, "append batch cap"); }
   { const int rows[2] = {5, 9};
+    const size_t wsb = lra_append_workspace_bytes(LRA_DTYPE_BF16, 2, 4096, 3, ranks);
+    assert(wsb > 0 && wsb != (size_t)-1);
+    assert(lra_append_workspace_bytes(LRA_DTYPE_F32, 2, 4096, 3, ranks) == 0);
+    assert(lra_append_workspace_bytes(LRA_DTYPE_BF16, -1, 4096, 3, ranks) == (size_t)-1);
     expect(lra_append_lr(LRA_DTYPE_BF16, 2, 4096, (void*)0x1000, 4096, (void*)0x2000, 192, 3, ranks,
-                         outs, ldl, rows, 100, nullptr), LRA_OK, "valid append"); }
+                         outs, ldl, rows, 100, nullptr, 0, nullptr), LRA_ERR_WORKSPACE,
+           "append without workspace");
+    expect(lra_append_lr(LRA_DTYPE_BF16, 2, 4096, (void*)0x1000, 4096, (void*)0x2000, 192, 3, ranks,
+                         outs, ldl, rows, 100, (void*)0x8000, wsb - 4, nullptr), LRA_ERR_WORKSPACE,
+           "append with a short workspace");
+    expect(lra_append_lr(LRA_DTYPE_BF16, 2, 4096, (void*)0x1000, 4096, (void*)0x2000, 192, 3, ranks,
+                         outs, ldl, rows, 100, (void*)0x8000, wsb, nullptr), LRA_OK, "valid append");
+    expect(lra_append_lr(LRA_DTYPE_F32, 2, 4096, (void*)0x1000, 4096, (void*)0x2000, 192, 3, ranks,
+                         outs, ldl, rows, 100, nullptr, 0, nullptr), LRA_OK, "fp32 append, no workspace"); }
+}
+
+// The bf16 append's split of d_model: slices of whole 256-value rounds that cover d_model
+// exactly once, partial blocks of 64 x 64 that cover the launch's tokens and columns, about
+// sixteen workgroups when that many rounds exist, and a workspace query that bounds every
+// launch of a call (batches above 256 tokens take several launches).
+static void check_append_plan() {
+  for (int64_t T : {1, 37, 64, 65, 256})
+    for (int64_t dm : {64, 128, 320, 512, 4096, 16384})
+      for (int64_t R : {8, 64, 192, 256}) {
+        const lra::AppendPlan p = lra::plan_append(T, dm, R);
+        const int nk = (int)(dm / 32);
+        assert(p.slice_chunks % 8 == 0 && p.slice_chunks > 0);
+        assert(p.n_slices >= 1 && p.n_slices <= lra::kAppendMaxSlices);
+        assert((int64_t)p.n_slices * p.slice_chunks >= nk);
+        assert((int64_t)(p.n_slices - 1) * p.slice_chunks < nk);   // no empty slice
+        assert(p.t_pad % 64 == 0 && p.t_pad >= T && p.t_pad < T + 64);
+        assert(p.r_pad % 64 == 0 && p.r_pad >= R && p.r_pad < R + 64);
+        const int64_t items = (int64_t)p.n_slices * (p.t_pad / 64) * (p.r_pad / 64);
+        assert(items >= std::min<int64_t>(16, (int64_t)((nk + 7) / 8) * (p.t_pad / 64) * (p.r_pad / 64)) / 2);
+      }
+  const lra::AppendPlan w = lra::plan_append(64, 4096, 64);   // the decode batch's append
+  assert(w.n_slices == 16 && w.slice_chunks == 8 && w.bytes() == 16 * 64 * 64 * 4);
+  const int ranks[6] = {0, 40, 24, 64, 64, 64};
+  void* outs[6] = {nullptr, (void*)0x10000, (void*)0x20000, (void*)0x30000, (void*)0x40000, (void*)0x50000};
+  const int64_t ldl[6] = {0, 40, 24, 64, 64, 64};
+  std::vector<int> rows(300);
+  for (int i = 0; i < 300; ++i) rows[i] = 2 * i;
+  const size_t wsb = lra_append_workspace_bytes(LRA_DTYPE_BF16, 300, 256, 6, ranks);
+  g_append.clear();
+  expect(lra_append_lr(LRA_DTYPE_BF16, 300, 256, (void*)0x1000, 256, (void*)0x2000, 256, 6, ranks,
+                       outs, ldl, rows.data(), 700, (void*)0x8000, wsb, nullptr), LRA_OK,
+         "append in two launches");
+  assert(g_append.size() == 2 && g_append[0].p.T == 256 && g_append[1].p.T == 44);
+  for (const lra::AppendArgs& a : g_append) {
+    const lra::AppendPlan p{a.n_slices, a.slice_chunks, a.t_pad, a.r_pad};
+    assert(a.part == (float*)0x8000 && (size_t)p.bytes() <= wsb);
+    assert(a.rows[0] == (a.p.T == 256 ? 0 : 512));
+  }
 }
 
 // The comparators: the in-tile expansion decode never groups shared contexts and launches
@@ -295,6 +347,7 @@ static void check_comparators() {
 int main() {
   check_validation();
   check_comparators();
+  check_append_plan();
   // prefill: a mixed batch (one launch), 100 requests (two launches), one request
   {
     std::vector<int> ql, kl;

@@ -197,7 +197,7 @@ def test_precompute_empty_is_noop():
 
 def _append(rows=(5, 0, 9), l_rows=10, batch=None, **kw):
     d = dict(dtype=lra.LRA_DTYPE_BF16, dm=64, X=FAKE, ldx=64, A=FAKE, lda=24, ranks=(8, 16),
-             L=(FAKE, FAKE + 4096), ldl=(8, 16))
+             L=(FAKE, FAKE + 4096), ldl=(8, 16), ws=FAKE, ws_bytes=1 << 20)
     d.update(kw)
     batch = len(rows) if batch is None else batch
     I = (ctypes.c_int32 * len(d["ranks"]))(*d["ranks"])
@@ -209,7 +209,7 @@ def _append(rows=(5, 0, 9), l_rows=10, batch=None, **kw):
                                ctypes.cast(P, ctypes.POINTER(ctypes.c_void_p)),
                                ctypes.cast(LD, ctypes.POINTER(ctypes.c_int64)),
                                ctypes.cast(RW, ctypes.POINTER(ctypes.c_int32)) if RW else None,
-                               l_rows, None)
+                               l_rows, d["ws"], d["ws_bytes"], None)
     return rc, lra.lra_last_error()
 
 
@@ -224,6 +224,9 @@ def _append(rows=(5, 0, 9), l_rows=10, batch=None, **kw):
     (dict(ranks=(8, 20)), lra.LRA_ERR_UNSUPPORTED, "multiples of 8"),
     (dict(L=(FAKE, None)), lra.LRA_ERR_INVALID, "null"),
     (dict(X=None), lra.LRA_ERR_INVALID, "non-null"),
+    (dict(ws=None, ws_bytes=0), lra.LRA_ERR_WORKSPACE, "workspace is null"),
+    (dict(ws_bytes=16), lra.LRA_ERR_WORKSPACE, "workspace of 16 bytes"),
+    (dict(ws=FAKE + 4), lra.LRA_ERR_INVALID, "16-byte aligned"),
 ])
 def test_append_rejections(kw, code, frag):
     rc, msg = _append(**kw)
@@ -232,7 +235,21 @@ def test_append_rejections(kw, code, frag):
 
 
 def test_append_empty_is_noop():
-    assert _append(rows=(), X=None, A=None)[0] == lra.LRA_OK
+    assert _append(rows=(), X=None, A=None, ws=None, ws_bytes=0)[0] == lra.LRA_OK
+
+
+def test_append_workspace_bytes():
+    ws = lra.lra_append_workspace_bytes
+    assert ws(lra.LRA_DTYPE_BF16, 64, 4096, (16, 16, 16, 16)) == 16 * 64 * 64 * 4
+    assert ws(lra.LRA_DTYPE_F32, 64, 4096, (16, 16, 16, 16)) == 0
+    assert ws(lra.LRA_DTYPE_BF16, 0, 4096, (16,)) == 0
+    assert ws(lra.LRA_DTYPE_BF16, 64, 4096, (0, 0)) == 0
+    assert ws(lra.LRA_DTYPE_BF16, 300, 256, (0, 40, 24, 64, 64, 64)) >= 256 * 256 * 4
+    with pytest.raises(lra.LraError):
+        ws(lra.LRA_DTYPE_BF16, -1, 4096, (16,))
+    # one byte short of that size is refused before anything is queued
+    n = ws(lra.LRA_DTYPE_BF16, 3, 64, (8, 16))
+    assert _append(ws_bytes=n - 1)[0] == lra.LRA_ERR_WORKSPACE
 
 
 def test_decode_rejections():

@@ -364,6 +364,8 @@ def test_precompute_into_rows_of_odd_stride():
     ("bf16", 37, 512, (64, 64, 64), 300),          # ragged token block, R = 192
     ("bf16", 1, 128, (8,), 5),                     # one token, one column block
     ("bf16", 300, 256, (0, 40, 24, 64, 64, 64), 700),   # two launches, R = 256, rank 0
+    ("bf16", 256, 4096, (64, 64, 64, 64), 600),    # 16 output blocks: one slice of 16 rounds
+    ("bf16", 64, 16384, (16, 16, 16, 16), 100),    # 16 slices of 4 rounds each
     ("f32", 20, 136, (8, 24), 50),
 ])
 def test_append_lr(dtype, batch, dm, ranks, l_rows):
@@ -391,4 +393,33 @@ def test_append_lr(dtype, batch, dm, ranks, l_rows):
         assert np.all(np.abs(got[rows] - want[a]) <= bound + 1e-30), f"agent {a}"
         assert np.isnan(got[others]).all(), f"agent {a}: rows outside `rows` were written"
         assert torch.equal(outs[a][rows], again[a][rows]), "repeat call not bitwise identical"
+
+
+def test_append_lr_reads_only_d_model_columns_and_reuses_workspace():
+    """X is a column block of a wider NaN-filled buffer and d_model (320) ends inside a
+    256-value round: the chunks past d_model must read zeros, not the padding.  A caller
+    workspace, dirty from an earlier call, serves two calls of different sizes."""
+    import oracle
+    from shared_rank_kv_amd import inputs, lra
+    dm, ranks = 320, (8, 16, 24)
+    p = workloads.PrecomputeProblem("append-pad", "bf16", 70, dm, ranks, seed=733)
+    X = p.X()
+    A = [p.A(a) for a in range(len(ranks))]
+    A_cat = torch.cat(A, dim=1).contiguous().cuda()
+    wide = torch.full((70, dm + 64), float("nan"), dtype=torch.bfloat16, device="cuda")
+    wide[:, :dm] = X.cuda()
+    need = max(lra.lra_append_workspace_bytes(torch.bfloat16, n, dm, ranks) for n in (70, 9))
+    ws = torch.full((need // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    want = oracle.lr_precompute(inputs.to_f64(X), [inputs.to_f64(a) for a in A])
+    for n in (70, 9):
+        rows = np.arange(n) * 3 + 1
+        outs = [torch.full((300, r), float("nan"), dtype=torch.bfloat16, device="cuda")
+                for r in ranks]
+        lra.lra_append_lr(wide[:n, :dm], A_cat, ranks, outs, rows, workspace=ws)
+        torch.cuda.synchronize()
+        for a in range(len(ranks)):
+            got = outs[a].double().cpu().numpy()[rows]
+            bound = dm * 2.0 ** -23 * (np.abs(inputs.to_f64(X[:n])) @ np.abs(inputs.to_f64(A[a])))
+            bound = bound + 2.0 ** -8 * np.abs(want[a][:n])
+            assert np.all(np.abs(got - want[a][:n]) <= bound + 1e-30), f"n {n} agent {a}"
 
