@@ -338,12 +338,16 @@ __global__ __launch_bounds__(512, 1) void fla_prefill_bf16(const AttnArgs args) 
   float m_run = kNegBig, l_run = 0.f;
   const float sl2 = A->scale_log2;
   f32x16 s[2];
-  bf16x8 pf[4];   // P of the previous tile as B operands, 16 keys each
+  bf16x8 pf[4] = {};   // P of the previous tile as B operands, 16 keys each (tile -1: zero)
 
-  // matrix phase M(j): PV(j-1) from vbuf, then Sᵀ(j) from kbuf
+  // matrix phase M(j): PV(j-1) from vbuf, then Sᵀ(j) from kbuf.  Both parts run in every
+  // step: step 0's P·V adds P = 0 times the zeroed rows of "tile -1", and the last step's
+  // scores (j == n_tiles, from a stale K tile) are never used.  Without the conditions the
+  // compiler keeps the LDS reads ahead of the MFMAs in all three unrolled steps (with them,
+  // one step of the rank > 32 kernel waited on every read).
   auto mma_phase = [&](int j, const LDS char* kbuf, const LDS char* vbuf) {
     if (!wave_active) return;
-    if (j >= 1) {
+    {
       const LDS char* vt = vbuf + TILE_KV;
       const LDS char* lt = vbuf + 2 * TILE_KV;
 #pragma unroll
@@ -366,7 +370,7 @@ __global__ __launch_bounds__(512, 1) void fla_prefill_bf16(const AttnArgs args) 
       }
       __builtin_amdgcn_sched_group_barrier(0x008, NM - (NR - kPfReads) / 2, 0);
     }
-    if (j < n_tiles) {
+    {
       // the two 32-key blocks alternate, so consecutive MFMAs are independent
       s[0] = f32x16{};
       s[1] = f32x16{};
@@ -497,6 +501,10 @@ __global__ __launch_bounds__(512, 1) void fla_prefill_bf16(const AttnArgs args) 
     lds_barrier();
   };
 
+  // the first step's P·V reads "tile -1" from buf2 with P = 0: its V and L rows are zeroed
+  // (uninitialised LDS could hold NaN patterns)
+  for (int o = tid * 16; o < BUF - TILE_KV; o += 512 * 16)
+    *(LDS f32x4*)(buf2 + TILE_KV + o) = f32x4{0.f, 0.f, 0.f, 0.f};
   // prologue: K(0), K(1) and V(0) before phase 0; B issues V(1) in its extra phase 0
   if (!group_b) {
     if (n_tiles > 0) load_k(kb, buf0);
