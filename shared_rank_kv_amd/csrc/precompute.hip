@@ -8,8 +8,8 @@
 // L_catᵀ = A_catᵀ·Xᵀ with v_mfma_f32_16x16x32_bf16, so that X is the B operand: in that
 // operand a lane holds eight consecutive d_model values of one token, which is 16
 // contiguous bytes of an X row.  X therefore streams from HBM straight into MFMA operand
-// registers and never touches LDS; it is fetched in visits of four 64-value chunks (512
-// contiguous bytes of each row), one visit ahead.  A_cat (small, L2-resident) is the A
+// registers and never touches LDS; each step issues one 64-value chunk (128 bytes of each
+// row), four chunks ahead.  A_cat (small, L2-resident) is the A
 // operand: it travels by direct buffer->LDS loads into a ring of four LDS tiles, three
 // chunks ahead, and is read back with the transposing LDS read.  Each workgroup owns 128
 // tokens and all R columns, so X is read from HBM exactly once; the epilogue rounds to
@@ -110,9 +110,9 @@ __global__ __launch_bounds__(256, 1) void lr_precompute_bf16(const PrecomputeArg
   constexpr int NB = 2;                        // 16-token blocks per wave (32 tokens)
   constexpr int MB = NCB;                      // 16-column blocks (all of R)
   constexpr int XN = NB * 2;                   // X loads per wave per chunk (2 k-steps)
-  constexpr int XV = 4;                        // chunks per X visit (512 bytes of each row)
+  constexpr int XV = 4;                        // granularity of the per-XCD chunk rotation
   constexpr int NT = 4;                        // A_cat tiles in the LDS ring
-  constexpr int UNROLL = 2 * XV;               // chunk steps per loop pass (two X visits)
+  constexpr int UNROLL = 8;                    // chunk steps per loop pass (X ring slots)
   static_assert(NAW * 4 * 1024 == ATILE, "tile split over four waves");
   static_assert(UNROLL % NT == 0, "static tile indices");
   // A_cat ring: chunk kc lives in tile kc % NT.  Separate arrays let the compiler see that
@@ -145,7 +145,8 @@ __global__ __launch_bounds__(256, 1) void lr_precompute_bf16(const PrecomputeArg
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) xoff[nb] = (int)((nb * 16 + col) * ldx * 2) + grp * 16;
   // The workgroups of one XCD sweep d_model in the same order, so each A_cat chunk is read
-  // into that XCD's L2 once and serves all of them; the eight XCDs start eight visits apart.
+  // into that XCD's L2 once and serves all of them; the eight XCDs start an eighth of
+  // d_model apart (rounded down to four chunks).
   const int rot = (int)(blockIdx.x & 7) * (nk >> 3) & ~(XV - 1);
   auto chunk = [&](int kc) { return kc < nk ? (kc + rot < nk ? kc + rot : kc + rot - nk) : 0; };
   u32x4 xop[UNROLL][NB][2];
@@ -197,15 +198,20 @@ __global__ __launch_bounds__(256, 1) void lr_precompute_bf16(const PrecomputeArg
     for (int cb = 0; cb < MB; ++cb) acc[nb][cb] = f32x4{};
 
   // Issue order per chunk step kc, before its MFMAs: A_cat chunk kc + 3 (into the tile chunk
-  // kc - 1 used), then, on every fourth step, the X visit of chunks kc + 4 .. kc + 7.  At the end of step
-  // kc the tile of chunk kc + 1 must be complete: issued two steps earlier, it was followed
-  // by two more tiles and, unless kc % 4 == 3, by one X visit, all of which may stay in
-  // flight.  The prologue issues the same sequence for the virtual steps -4 .. -1.
+  // kc - 1 used), then the X operands of chunk kc + 4, so X streams as a sliding window of
+  // four chunks.  At the end of step kc the tile and the X operands of chunk kc + 1 must be
+  // complete; both precede A_cat chunk kc + 1 in issue order, which was followed by X of
+  // kc + 2, A of kc + 2, X of kc + 3, A of kc + 3 and X of kc + 4: those may stay in flight.
+  // (Issuing X a whole visit of four chunks at a time made each visit's wait cover all four
+  // chunks at once; measured 2-3 % slower.)  The prologue issues X(0) A(0) X(1) A(1) X(2)
+  // A(2) X(3).
 #pragma unroll
-  for (int i = 0; i < XV; ++i) load_x(xop[i], i);
-#pragma unroll
-  for (int i = 0; i < NT - 1; ++i) load_a(tiles[i], i);
-  wait_vm<2 * NAW>();
+  for (int i = 0; i < NT - 1; ++i) {
+    load_x(xop[i], i);
+    load_a(tiles[i], i);
+  }
+  load_x(xop[NT - 1], NT - 1);
+  wait_vm<3 * XN + 2 * NAW>();
   lds_barrier();
 
   for (int kc0 = 0; kc0 < nk_pad; kc0 += UNROLL) {
@@ -217,10 +223,7 @@ __global__ __launch_bounds__(256, 1) void lr_precompute_bf16(const PrecomputeArg
       // kc - 1 and the X slots of chunks kc - 4 .. kc - 1 are free (the barrier that ended
       // step kc - 1 follows every read of them)
       load_a(tiles[(st + NT - 1) % NT], kc + NT - 1);
-      if (st % XV == 0) {
-#pragma unroll
-        for (int i = 0; i < XV; ++i) load_x(xop[(st + XV + i) % UNROLL], kc + XV + i);
-      }
+      load_x(xop[(st + NT) % UNROLL], kc + NT);
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         bf16x8 aop[MB];
@@ -236,8 +239,7 @@ __global__ __launch_bounds__(256, 1) void lr_precompute_bf16(const PrecomputeArg
             acc[nb][cb] = mfma16(aop[cb], __builtin_bit_cast(bf16x8, xop[st][nb][ks]),
                                  acc[nb][cb]);
       }
-      if (st % XV == XV - 1) wait_vm<2 * NAW>();
-      else wait_vm<2 * NAW + XV * XN>();
+      wait_vm<3 * XN + 2 * NAW>();
       lds_barrier();
     }
   }
