@@ -137,3 +137,35 @@ def test_graph_capture_and_replay(lra, monkeypatch):
         assert torch.equal(O_p, want_p), f"prefill differs on replay {rep}"
         assert torch.equal(O_d, want_d), f"decode differs on replay {rep}"
     del g
+
+
+def test_append_graph_capture_and_replay(lra):
+    """The two-pass bf16 append (slice partials in a caller workspace, then the ordered
+    sums) captured into a graph: every replay writes the eager result, bitwise, with an
+    eager call that reuses the workspace between replays."""
+    p = workloads.PrecomputeProblem("graph-append", "bf16", 64, 4096, (16, 16, 16, 16), seed=702)
+    X = p.X().cuda()
+    A_cat = torch.cat([p.A(a) for a in range(4)], 1).contiguous().cuda()
+    rows = np.arange(64) * 7 + 3
+    outs = [torch.zeros(500, 16, dtype=torch.bfloat16, device="cuda") for _ in range(4)]
+    ws = torch.empty(lra.lra_append_workspace_bytes(torch.bfloat16, 64, 4096, (16,) * 4),
+                     dtype=torch.uint8, device="cuda")
+    fa = lra.prepare_append_lr(X, A_cat, (16,) * 4, outs, rows, workspace=ws)
+    fa()
+    torch.cuda.synchronize()
+    want = [o.clone() for o in outs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fa()
+    for rep in range(4):
+        for o in outs:
+            o.zero_()
+        fa()
+        torch.cuda.synchronize()
+        for o in outs:
+            o.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for a in range(4):
+            assert torch.equal(outs[a], want[a]), f"agent {a} differs on replay {rep}"
+    del g
