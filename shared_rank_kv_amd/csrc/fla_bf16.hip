@@ -223,9 +223,12 @@ constexpr int kPfReads = 18;
 // M(j), and attention runs without an adapter term.  B then waits for V(j+1) at the end of
 // its softmax phase (three phases of latency, like K), so the tile is complete when the
 // expansion starts.
+// One work item w (of request b) of the prefill; the three rotating tile buffers (and, for
+// EX, the B_g tile) are the calling kernel's LDS, sized for at least this RB.
 template <int D, int RB, bool EX>
-__global__ __launch_bounds__(512, 1) void fla_prefill_bf16(const AttnArgs args) {
-  const AttnArgs* A = (const AttnArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+__device__ __forceinline__ void prefill_item(const AttnArgs* A, const int w, const int b,
+                                             LDS char* const buf0, LDS char* const buf1,
+                                             LDS char* const buf2, LDS char* const btile) {
   constexpr int DB = D / 32;
   constexpr int KS = D / 16;
   constexpr int TILE_KV = 64 * D * 2;
@@ -233,22 +236,6 @@ __global__ __launch_bounds__(512, 1) void fla_prefill_bf16(const AttnArgs args) 
   constexpr int BUF = 2 * TILE_KV + (RB ? TILE_L : 0);
   constexpr int RBA = EX ? 0 : RB;     // rank blocks of the attention's LR term
   constexpr int kRows = kPrefillRows;
-  __shared__ __attribute__((aligned(1024))) char smem0[BUF];
-  __shared__ __attribute__((aligned(1024))) char smem1[BUF];
-  __shared__ __attribute__((aligned(1024))) char smem2[BUF];
-  __shared__ __attribute__((aligned(1024))) char smemb[EX ? TILE_KV : 16];
-  LDS char* const buf0 = (LDS char*)smem0;
-  LDS char* const buf1 = (LDS char*)smem1;
-  LDS char* const buf2 = (LDS char*)smem2;
-  LDS char* const btile = (LDS char*)smemb;
-
-  const int bid = blockIdx.x;
-  const int w = A->grid_per_xcd > 0
-                    ? (bid & 7) * A->grid_per_xcd + (bid >> 3)
-                    : ((bid >> 3) / kDealChunk) * (8 * kDealChunk) + (bid & 7) * kDealChunk +
-                          (bid >> 3) % kDealChunk;
-  if (w >= A->n_work) return;
-  const int b = find_request(A, w);
   const ReqDesc& R = A->reqs[b];
   const int q_start = R.q_start, Lq = R.q_len, k_start = R.k_start, Lk = R.k_len;
   const int n_rt = R.n_rt, n_split = R.n_split;
@@ -589,6 +576,55 @@ __global__ __launch_bounds__(512, 1) void fla_prefill_bf16(const AttnArgs args) 
   }
 }
 
+// blockIdx -> work item: XCD-major for one request (grid_per_xcd > 0), else dealt in
+// chunks of kDealChunk items round-robin over the XCDs
+__device__ __forceinline__ int prefill_work_item(const AttnArgs* A) {
+  const int bid = blockIdx.x;
+  return A->grid_per_xcd > 0
+             ? (bid & 7) * A->grid_per_xcd + (bid >> 3)
+             : ((bid >> 3) / kDealChunk) * (8 * kDealChunk) + (bid & 7) * kDealChunk +
+                   (bid >> 3) % kDealChunk;
+}
+
+template <int D, int RB, bool EX>
+__global__ __launch_bounds__(512, 1) void fla_prefill_bf16(const AttnArgs args) {
+  const AttnArgs* A = (const AttnArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+  constexpr int TILE_KV = 64 * D * 2;
+  constexpr int BUF = 2 * TILE_KV + (RB ? 64 * 64 * 2 : 0);
+  __shared__ __attribute__((aligned(1024))) char smem0[BUF];
+  __shared__ __attribute__((aligned(1024))) char smem1[BUF];
+  __shared__ __attribute__((aligned(1024))) char smem2[BUF];
+  __shared__ __attribute__((aligned(1024))) char smemb[EX ? TILE_KV : 16];
+  const int w = prefill_work_item(A);
+  if (w >= A->n_work) return;
+  prefill_item<D, RB, EX>(A, w, find_request(A, w), (LDS char*)smem0, (LDS char*)smem1,
+                          (LDS char*)smem2, (LDS char*)smemb);
+}
+
+// A launch whose requests span LR widths (ranks 0, up to 32 and up to 64): each work item
+// runs the loop of its own agent's width, so a rank-16 request next to rank-64 ones does
+// not pay for the wider LR term (in one launch, without a second launch's tail).
+template <int D>
+__global__ __launch_bounds__(512, 1) void fla_prefill_mixed_bf16(const AttnArgs args) {
+  const AttnArgs* A = (const AttnArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+  constexpr int BUF = 2 * 64 * D * 2 + 64 * 64 * 2;
+  __shared__ __attribute__((aligned(1024))) char smem0[BUF];
+  __shared__ __attribute__((aligned(1024))) char smem1[BUF];
+  __shared__ __attribute__((aligned(1024))) char smem2[BUF];
+  __shared__ __attribute__((aligned(1024))) char smemb[16];
+  const int w = prefill_work_item(A);
+  if (w >= A->n_work) return;
+  const int b = find_request(A, w);
+  const int rank = __builtin_amdgcn_readfirstlane(A->agents[A->reqs[b].agent].rank);
+  LDS char* const b0 = (LDS char*)smem0;
+  LDS char* const b1 = (LDS char*)smem1;
+  LDS char* const b2 = (LDS char*)smem2;
+  LDS char* const bt = (LDS char*)smemb;
+  if (rank > 32) prefill_item<D, 2, false>(A, w, b, b0, b1, b2, bt);
+  else if (rank > 0) prefill_item<D, 1, false>(A, w, b, b0, b1, b2, bt);
+  else prefill_item<D, 0, false>(A, w, b, b0, b1, b2, bt);
+}
+
 // Merge the key-split states of one output row:
 //   M = max m_s, w_s = 2^(m_s - M),   O = Σ w_s·acc_s / Σ w_s·l_s
 // where acc_s = (P·V_base)_s + (P·L)_s·B_g already holds the up-projection (B is linear).
@@ -672,8 +708,16 @@ __global__ __launch_bounds__(256) void fla_combine_bf16(const AttnArgs args) {
 }  // namespace
 
 hipError_t launch_prefill_bf16(const AttnArgs& a, int head_dim, int max_rank, int n_grid,
-                               hipStream_t s, bool expand) {
+                               hipStream_t s, bool expand, int min_rank) {
   const int rb = max_rank > 32 ? 2 : (max_rank > 0 ? 1 : 0);
+  const int rb_lo = min_rank < 0 ? rb : (min_rank > 32 ? 2 : (min_rank > 0 ? 1 : 0));
+  if (!expand && rb_lo != rb) {        // the launch spans LR widths
+    if (head_dim == 128)
+      hipLaunchKernelGGL((fla_prefill_mixed_bf16<128>), dim3(n_grid), dim3(512), 0, s, a);
+    else
+      hipLaunchKernelGGL((fla_prefill_mixed_bf16<64>), dim3(n_grid), dim3(512), 0, s, a);
+    return hipGetLastError();
+  }
 #define LRA_LAUNCH(D, RB, EX) \
   hipLaunchKernelGGL((fla_prefill_bf16<D, RB, EX>), dim3(n_grid), dim3(512), 0, s, a)
   if (expand && rb > 0) {

@@ -407,10 +407,13 @@ int run_attention(const AttnShape& s, bool decode, const Requests& rq, const voi
       const int64_t round = dealt ? 8 * lra::kDealChunk : 8;
       const int grid = (int)(ceil_div(work, round) * round);
       a.grid_per_xcd = dealt ? 0 : grid / 8;
-      int max_rank = 0;
-      for (size_t i = c0; i < c1; ++i) max_rank = std::max(max_rank, ad.ranks[rq.agent[p.active[i]]]);
+      int max_rank = 0, min_rank = LRA_MAX_RANK;
+      for (size_t i = c0; i < c1; ++i) {
+        max_rank = std::max(max_rank, ad.ranks[rq.agent[p.active[i]]]);
+        min_rank = std::min(min_rank, ad.ranks[rq.agent[p.active[i]]]);
+      }
       if (!decode)
-        e = lra::launch_prefill_bf16(a, s.D, max_rank, grid, stream, expand);
+        e = lra::launch_prefill_bf16(a, s.D, max_rank, grid, stream, expand, min_rank);
       else if (shared)
         e = lra::launch_decode_shared_bf16(a, s.D, max_rank, grid, stream);
       else

@@ -129,8 +129,10 @@ struct ExpandArgs {
 int report_error(int code, const char* msg);
 
 // Launchers (return the HIP status of the launch).
+// min_rank: the smallest rank among the launch's requests (-1: not known); a launch whose
+// ranks span LR widths runs each work item at its own width.
 hipError_t launch_prefill_bf16(const AttnArgs& a, int head_dim, int max_rank, int n_grid,
-                               hipStream_t s, bool expand = false);
+                               hipStream_t s, bool expand = false, int min_rank = -1);
 hipError_t launch_decode_shared_bf16(const AttnArgs& a, int head_dim, int max_rank, int n_grid,
                                      hipStream_t s);
 // expand: the in-tile expansion comparator (each V_base tile expanded with L·B_g in LDS

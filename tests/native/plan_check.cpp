@@ -21,7 +21,7 @@ static std::vector<Rec> g_recs;
 static std::vector<lra::ExpandArgs> g_expand;
 static std::vector<lra::AppendArgs> g_append;
 namespace lra {
-hipError_t launch_prefill_bf16(const AttnArgs& a, int, int, int grid, hipStream_t, bool ex) { g_recs.push_back({a, 0, grid, ex}); return hipSuccess; }
+hipError_t launch_prefill_bf16(const AttnArgs& a, int, int, int grid, hipStream_t, bool ex, int) { g_recs.push_back({a, 0, grid, ex}); return hipSuccess; }
 hipError_t launch_decode_bf16(const AttnArgs& a, int, int, int, hipStream_t, bool ex) { g_recs.push_back({a, 1, 0, ex}); return hipSuccess; }
 hipError_t launch_expand_bf16(const ExpandArgs& a, int, int, hipStream_t) { g_expand.push_back(a); return hipSuccess; }
 hipError_t launch_decode_shared_bf16(const AttnArgs& a, int, int, int, hipStream_t) { g_recs.push_back({a, 2, 0, false}); return hipSuccess; }
