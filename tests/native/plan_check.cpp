@@ -16,12 +16,12 @@
 #include "lra.h"
 #include "lra_internal.h"
 
-struct Rec { lra::AttnArgs a; int kind; int grid; bool expand; };   // 0 prefill, 1 decode, 2 decode shared, 3 combine, 4 f32
+struct Rec { lra::AttnArgs a; int kind; int grid; bool expand; int min_rank = -1; };   // 0 prefill, 1 decode, 2 decode shared, 3 combine, 4 f32
 static std::vector<Rec> g_recs;
 static std::vector<lra::ExpandArgs> g_expand;
 static std::vector<lra::AppendArgs> g_append;
 namespace lra {
-hipError_t launch_prefill_bf16(const AttnArgs& a, int, int, int grid, hipStream_t, bool ex, int) { g_recs.push_back({a, 0, grid, ex}); return hipSuccess; }
+hipError_t launch_prefill_bf16(const AttnArgs& a, int, int, int grid, hipStream_t, bool ex, int min_rank) { g_recs.push_back({a, 0, grid, ex, min_rank}); return hipSuccess; }
 hipError_t launch_decode_bf16(const AttnArgs& a, int, int, int, hipStream_t, bool ex) { g_recs.push_back({a, 1, 0, ex}); return hipSuccess; }
 hipError_t launch_expand_bf16(const ExpandArgs& a, int, int, hipStream_t) { g_expand.push_back(a); return hipSuccess; }
 hipError_t launch_decode_shared_bf16(const AttnArgs& a, int, int, int, hipStream_t) { g_recs.push_back({a, 2, 0, false}); return hipSuccess; }
@@ -94,20 +94,22 @@ static int check(int batch, int Hq, int Hkv, const std::vector<int>& ks, const s
 // (ceil(k_len / n_split)) and dealt over the XCDs (grid_per_xcd == 0); a single request
 // keeps the XCD-major mapping.  Either way the kernel's block -> item map covers every
 // work item exactly once, and every request appears exactly once.
-static int check_prefill_order(const std::vector<int>& ql, const std::vector<int>& kl) {
+static int check_prefill_order(const std::vector<int>& ql, const std::vector<int>& kl,
+                               const std::vector<int>& ranks = {16},
+                               const std::vector<int>& agents = {}) {
   g_recs.clear();
   const int batch = (int)ql.size(), Hq = 32, Hkv = 8;
   std::vector<int> qs(batch), ks(batch), ag(batch, 0);
+  for (int b = 0; b < batch && !agents.empty(); ++b) ag[b] = agents[b];
   int64_t q_rows = 0, kv_rows = 0;
   for (int b = 0; b < batch; ++b) { qs[b] = (int)q_rows; q_rows += ql[b]; ks[b] = (int)kv_rows; kv_rows += kl[b]; }
-  std::vector<int> ranks = {16};
-  std::vector<const void*> L = {(void*)0x100000}, B = {(void*)0x200000};
-  std::vector<int64_t> ldl = {16};
-  const size_t wsb = lra_attn_workspace_bytes(LRA_DTYPE_BF16, 0, batch, ql.data(), kl.data(), Hq, Hkv, 128, 16);
+  std::vector<const void*> L(ranks.size(), (void*)0x100000), B(ranks.size(), (void*)0x200000);
+  std::vector<int64_t> ldl(ranks.size(), 64);
+  const size_t wsb = lra_attn_workspace_bytes(LRA_DTYPE_BF16, 0, batch, ql.data(), kl.data(), Hq, Hkv, 128, 64);
   int rc = lra_attn_prefill(LRA_DTYPE_BF16, batch, Hq, Hkv, 128, qs.data(), ql.data(), ks.data(),
                             kl.data(), ag.data(), (void*)0x1000, q_rows, (void*)0x2000, (void*)0x3000,
-                            kv_rows, 1, ranks.data(), L.data(), ldl.data(), B.data(), (void*)0x4000,
-                            wsb ? (void*)0x10000000 : nullptr, wsb, nullptr);
+                            kv_rows, (int)ranks.size(), ranks.data(), L.data(), ldl.data(), B.data(),
+                            (void*)0x4000, wsb ? (void*)0x10000000 : nullptr, wsb, nullptr);
   if (rc) { printf("rc %d: %s\n", rc, lra_last_error()); return 1; }
   std::multiset<int> seen;
   for (const Rec& r : g_recs) {
@@ -125,6 +127,10 @@ static int check_prefill_order(const std::vector<int>& ql, const std::vector<int
     }
     assert(work == a.n_work);
     assert((a.n_req > 1) == (a.grid_per_xcd == 0));
+    // the launch reports its smallest rank (the kernel then runs each item at its own width)
+    int lo = 1 << 30;
+    for (int i = 0; i < a.n_req; ++i) lo = std::min(lo, a.agents[a.reqs[i].agent].rank);
+    assert(r.min_rank == lo);
     std::vector<int> hit(a.n_work, 0);
     for (int bid = 0; bid < r.grid; ++bid) {
       const int w = a.grid_per_xcd > 0
@@ -357,6 +363,12 @@ int main() {
     for (int i = 0; i < 100; ++i) { ql.push_back(1 + (i * 37) % 300); kl.push_back(ql.back() + (i * 911) % 5000); }
     assert(!check_prefill_order(ql, kl));
     assert(!check_prefill_order({1024}, {9216}));
+    // agents of ranks 8, 64 and 0 in one launch
+    {
+      std::vector<int> mq, mk, ma;
+      for (int i = 0; i < 12; ++i) { mq.push_back(1 + (i * 53) % 300); mk.push_back(mq.back() + 500 + (i * 977) % 4000); ma.push_back(i % 3); }
+      assert(!check_prefill_order(mq, mk, {8, 64, 0}, ma));
+    }
   }
   // 16 contexts x 4 agents, G = 4: units of 4
   {
