@@ -423,3 +423,37 @@ def test_append_lr_reads_only_d_model_columns_and_reuses_workspace():
             bound = bound + 2.0 ** -8 * np.abs(want[a][:n])
             assert np.all(np.abs(got - want[a][:n]) <= bound + 1e-30), f"n {n} agent {a}"
 
+
+
+# ---------------------------------------------------------------------------------------
+# Maximum sizes: LRA_MAX_BATCH requests in one call (several launches of at most 64
+# requests each) over LRA_MAX_AGENTS agents of every rank 0..64
+# ---------------------------------------------------------------------------------------
+
+MAX_RANKS = (0, 8, 16, 24, 32, 40, 48, 56, 64, 8, 16, 32, 64, 0, 48, 16)
+
+
+def _max_problem(dtype, decode, D, Hq, Hkv, seed):
+    from shared_rank_kv_amd import lra
+    n = 1024
+    assert len(MAX_RANKS) == 16
+    rng = np.random.default_rng(seed)
+    k_len = [int(k) for k in rng.integers(1, 160, n)]
+    q_len = [1] * n if decode else [int(rng.integers(0, min(k, 5) + 1)) for k in k_len]
+    agents = [int(a) for a in rng.integers(0, 16, n)]
+    return workloads.custom(f"max-{dtype}-{'dec' if decode else 'pre'}", dtype, Hq, Hkv, D,
+                            MAX_RANKS, q_len, k_len, agents, seed=seed)
+
+
+@pytest.mark.parametrize("decode", [False, True], ids=["prefill", "decode"])
+def test_bf16_max_batch_and_agents(decode):
+    prob = _max_problem("bf16", decode, 128, 32, 8, seed=780 + decode)
+    cpu, dev = H.device_inputs(prob)
+    O = H.run_decode(prob, dev) if decode else H.run_prefill(prob, dev)
+    _cmp_full(prob, cpu, O)
+
+
+def test_fp32_max_batch_and_agents():
+    prob = _max_problem("f32", False, 64, 8, 2, seed=790)
+    cpu, dev = H.device_inputs(prob)
+    _cmp_full(prob, cpu, H.run_prefill(prob, dev), bf16=False)
