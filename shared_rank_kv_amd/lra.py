@@ -126,6 +126,26 @@ def _like(t, ref, name):
                          f"(got {t.dtype} on {t.device})")
 
 
+def _attn_tensors(Q, K_base, V_base, O=None):
+    """Checks of the attention operands the C ABI cannot see: shapes, dtypes and devices of
+    Q [rows, Hq, D], K_base and V_base [kv_rows, Hkv, D] and a caller's O (Q's shape); the
+    GPU check comes last."""
+    for t, name in ((Q, "Q"), (K_base, "K_base"), (V_base, "V_base")):
+        if t.dim() != 3:
+            raise ValueError(f"{name} must be 3-D [rows, heads, head_dim] (got {tuple(t.shape)})")
+    _like(K_base, Q, "K_base"), _like(V_base, Q, "V_base")
+    if V_base.shape != K_base.shape or K_base.shape[2] != Q.shape[2]:
+        raise ValueError(f"K_base {tuple(K_base.shape)} and V_base {tuple(V_base.shape)} must "
+                         f"share one shape with Q's head_dim {Q.shape[2]}")
+    if O is not None:
+        _like(O, Q, "O")
+        if O.shape != Q.shape:
+            raise ValueError(f"O {tuple(O.shape)} must have Q's shape {tuple(Q.shape)}")
+    _dev(Q, "Q"), _dev(K_base, "K_base"), _dev(V_base, "V_base")
+    if O is not None:
+        _dev(O, "O")
+
+
 def _adapter_ranks(Q, L, B, kv_rows, Hkv, D):
     """Checks every agent's LR cache and up-projection against the call (the C ABI cannot
     see dtypes, devices or a transposed view) and returns the ranks.  L[a] is None (rank 0)
@@ -153,8 +173,11 @@ def _adapter_ranks(Q, L, B, kv_rows, Hkv, D):
     return ranks
 
 
-def _lr_outputs(X, A_cat, ranks, L_out):
-    """Checks of the precompute / append operands the C ABI cannot see."""
+def _lr_outputs(X, A_cat, ranks, L_out, append=False):
+    """Checks of the precompute / append operands the C ABI cannot see; returns the LR
+    caches' row count.  The precompute writes X's rows to every cache, so each needs at
+    least that many; the append writes the listed rows, checked against one row count
+    that every cache must share."""
     if X.dim() != 2 or A_cat.dim() != 2 or X.stride(1) != 1 or A_cat.stride(1) != 1:
         raise ValueError("X and A_cat must be 2-D with unit column stride")
     _like(A_cat, X, "A_cat")
@@ -170,8 +193,14 @@ def _lr_outputs(X, A_cat, ranks, L_out):
         if t.dim() != 2 or t.stride(1) != 1 or t.shape[1] != int(r):
             raise ValueError(f"L_out[{a}] must be [rows, {r}] with unit column stride "
                              f"(got shape {tuple(t.shape)}, strides {t.stride()})")
+    counts = sorted({int(t.shape[0]) for t in L_out if t is not None})
+    if append and len(counts) > 1:
+        raise ValueError(f"L_out tensors must share one row count (got {counts})")
+    if not append and counts and counts[0] < X.shape[0]:
+        raise ValueError(f"L_out tensors need at least X's {X.shape[0]} rows (got {counts[0]})")
     if not X.is_cuda:
         raise ValueError("X must be a GPU tensor")
+    return counts[0] if counts else 0
 
 
 # ---------------------------------------------------------------------------------------
@@ -200,6 +229,8 @@ def _workspace(nbytes, device, workspace):
     if nbytes == 0:
         return None, 0
     if workspace is not None:
+        if workspace.device != device or not workspace.is_contiguous():
+            raise ValueError(f"workspace must be a contiguous tensor on {device}")
         return workspace, workspace.numel() * workspace.element_size()
     return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
 
@@ -269,12 +300,11 @@ def prepare_append_lr(X, A_cat, ranks, L_out, rows, workspace=None):
     lra_append_workspace_bytes bytes (allocated here when None).
     """
     _dtype(X)
-    _lr_outputs(X, A_cat, ranks, L_out)
+    l_rows = _lr_outputs(X, A_cat, ranks, L_out, append=True)
     rk, rkp = _i32(ranks)
     pk, ptrs = _ptrs(L_out)
     ld, ldp = _i64([t.stride(0) if t is not None else 0 for t in L_out])
     rw, rwp = _i32(rows)
-    l_rows = max([t.shape[0] for t in L_out if t is not None] + [0])
     need = lib.lra_append_workspace_bytes(_dtype(X), X.shape[0], X.shape[1], len(rk), rkp)
     if need == ctypes.c_size_t(-1).value:
         need = 0      # invalid arguments: the call reports why
@@ -296,8 +326,7 @@ def prepare_attn_prefill(Q, K_base, V_base, L, B, q_start, q_len, k_start, k_len
                          O=None, workspace=None, expand=False):
     """Prepared lra_attn_prefill (see lra_attn_prefill); expand=True prepares the in-tile
     expansion comparator lra_attn_prefill_expand instead."""
-    _dev(Q, "Q"), _dev(K_base, "K_base"), _dev(V_base, "V_base")
-    _like(K_base, Q, "K_base"), _like(V_base, Q, "V_base")
+    _attn_tensors(Q, K_base, V_base, O)
     dt = _dtype(Q)
     q_rows, Hq, D = Q.shape
     kv_rows, Hkv, _ = K_base.shape
@@ -343,8 +372,7 @@ def prepare_attn_decode(Q, K_base, V_base, L, B, k_start, k_len, agent_idx, O=No
                         workspace=None, expand=False):
     """Prepared lra_attn_decode (see lra_attn_decode); expand=True prepares the in-tile
     expansion comparator lra_attn_decode_expand instead."""
-    _dev(Q, "Q"), _dev(K_base, "K_base"), _dev(V_base, "V_base")
-    _like(K_base, Q, "K_base"), _like(V_base, Q, "V_base")
+    _attn_tensors(Q, K_base, V_base, O)
     dt = _dtype(Q)
     batch, Hq, D = Q.shape
     kv_rows, Hkv, _ = K_base.shape
@@ -384,8 +412,7 @@ def lra_attn_decode(Q, K_base, V_base, L, B, k_start, k_len, agent_idx, O=None, 
 def prepare_attn_decode_noalloc(Q, K_base, V_base, L, B, k_start, k_len, agent_idx, O):
     """Prepared lra_attn_decode_noalloc: the decode with the library's fixed scratch; O is
     the caller's output [batch, Hq, D] (nothing is allocated)."""
-    _dev(Q, "Q"), _dev(K_base, "K_base"), _dev(V_base, "V_base"), _dev(O, "O")
-    _like(K_base, Q, "K_base"), _like(V_base, Q, "V_base"), _like(O, Q, "O")
+    _attn_tensors(Q, K_base, V_base, O)
     dt = _dtype(Q)
     batch, Hq, D = Q.shape
     kv_rows, Hkv, _ = K_base.shape

@@ -318,3 +318,54 @@ def test_binding_checks_precompute_operands():
         with pytest.raises(ValueError) as e:
             lra._lr_outputs(x, a, (8, 16), o)
         assert frag in str(e.value), (frag, str(e.value))
+
+
+def test_binding_checks_lr_cache_rows():
+    """The precompute writes X's rows to every LR cache; the append checks its rows against
+    one row count, which every cache must then have (a shorter one would be written past
+    its end)."""
+    import torch
+    bf = torch.bfloat16
+    X = torch.zeros(10, 64, dtype=bf)
+    A = torch.zeros(64, 24, dtype=bf)
+    with pytest.raises(ValueError, match="at least X's 10 rows"):
+        lra._lr_outputs(X, A, (8, 16), [torch.zeros(10, 8, dtype=bf), torch.zeros(9, 16, dtype=bf)])
+    with pytest.raises(ValueError, match="share one row count"):
+        lra._lr_outputs(X, A, (8, 16), [torch.zeros(40, 8, dtype=bf), torch.zeros(30, 16, dtype=bf)],
+                        append=True)
+    # caches longer than X are fine for the precompute, and a rank-0 agent may have none
+    with pytest.raises(ValueError, match="X must be a GPU tensor"):
+        lra._lr_outputs(X, A, (8, 0, 16), [torch.zeros(12, 8, dtype=bf), None,
+                                           torch.zeros(10, 16, dtype=bf)])
+
+
+def test_binding_checks_attention_tensors():
+    import torch
+    bf = torch.bfloat16
+    Q = torch.zeros(4, 8, 128, dtype=bf)
+    K = torch.zeros(100, 2, 128, dtype=bf)
+    bad = [
+        (Q[0], K, K, None, "Q must be 3-D"),
+        (Q, K.float(), K, None, "K_base must be a torch.bfloat16"),
+        (Q, K, K[:90], None, "must share one shape"),
+        (Q, torch.zeros(100, 2, 64, dtype=bf), torch.zeros(100, 2, 64, dtype=bf), None,
+         "must share one shape"),
+        (Q, K, K, Q.float(), "O must be a torch.bfloat16"),
+        (Q, K, K, Q[:2], "must have Q's shape"),
+        (Q, K, K, Q, "Q must be a contiguous GPU tensor"),   # every other check passes
+    ]
+    for q, k, v, o, frag in bad:
+        with pytest.raises(ValueError) as e:
+            lra._attn_tensors(q, k, v, o)
+        assert frag in str(e.value), (frag, str(e.value))
+
+
+def test_binding_checks_caller_workspace():
+    import torch
+    with pytest.raises(ValueError, match="contiguous tensor on cuda:0"):
+        lra._workspace(256, torch.device("cuda", 0), torch.empty(256, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="contiguous tensor on cpu"):
+        lra._workspace(256, torch.device("cpu"), torch.empty(512, dtype=torch.uint8)[::2])
+    ws = torch.empty(300, dtype=torch.uint8)
+    assert lra._workspace(256, torch.device("cpu"), ws) == (ws, 300)
+    assert lra._workspace(0, torch.device("cpu"), ws) == (None, 0)
