@@ -130,7 +130,8 @@ int lra_append_lr(int dtype, int32_t batch, int64_t d_model,
 /*
  * lra_append_workspace_bytes -- scratch bytes lra_append_lr needs with these arguments
  * (ranks: host [n_agents]).  Returns 0 when no scratch is needed (fp32, batch 0, all ranks
- * 0), and (size_t)-1 when the arguments are invalid.
+ * 0), and (size_t)-1 when lra_append_lr would refuse them: a dtype, batch, agent count,
+ * rank, sum of ranks or d_model outside its rules.
  */
 size_t lra_append_workspace_bytes(int dtype, int32_t batch, int64_t d_model,
                                   int32_t n_agents, const int32_t* ranks);

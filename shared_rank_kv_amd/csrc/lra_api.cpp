@@ -813,11 +813,14 @@ size_t lra_append_workspace_bytes(int dtype, int32_t batch, int64_t d_model, int
       batch > LRA_MAX_BATCH || d_model <= 0 || n_agents <= 0 || n_agents > LRA_MAX_AGENTS ||
       !ranks)
     return (size_t)-1;
+  // the rank and size rules of lra_append_lr, so that no size is given for a call it refuses
   int64_t R = 0;
   for (int i = 0; i < n_agents; ++i) {
-    if (ranks[i] < 0) return (size_t)-1;
+    if (ranks[i] < 0 || ranks[i] > LRA_MAX_RANK || ranks[i] % 8 != 0) return (size_t)-1;
     R += ranks[i];
   }
+  if (R > 256 || d_model % 8 != 0 || (dtype == LRA_DTYPE_BF16 && d_model % 64 != 0))
+    return (size_t)-1;
   if (dtype != LRA_DTYPE_BF16 || batch == 0 || R == 0) return 0;
   return append_workspace(batch, d_model, R);
 }

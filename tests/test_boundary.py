@@ -247,6 +247,12 @@ def test_append_workspace_bytes():
     assert ws(lra.LRA_DTYPE_BF16, 300, 256, (0, 40, 24, 64, 64, 64)) >= 256 * 256 * 4
     with pytest.raises(lra.LraError):
         ws(lra.LRA_DTYPE_BF16, -1, 4096, (16,))
+    # arguments lra_append_lr refuses get no size either
+    for batch, dm, ranks in [(8, 4096, (12,)), (8, 4096, (72,)), (8, 4096, (-8,)),
+                             (8, 4096, (64, 64, 64, 64, 8)), (8, 4000, (16,)), (8, 4100, (16,))]:
+        with pytest.raises(lra.LraError):
+            ws(lra.LRA_DTYPE_BF16, batch, dm, ranks)
+    assert ws(lra.LRA_DTYPE_F32, 8, 4000, (16,)) == 0       # fp32 only needs d_model % 8
     # one byte short of that size is refused before anything is queued
     n = ws(lra.LRA_DTYPE_BF16, 3, 64, (8, 16))
     assert _append(ws_bytes=n - 1)[0] == lra.LRA_ERR_WORKSPACE
