@@ -122,14 +122,14 @@ def time_calls(fn, steps, warmup, flush=None):
 # what the same counter reads for a plain 1 GiB device copy); the per-kernel summaries and
 # the commands are under profiles/.  The figures describe the kernels built from sources
 # with this digest and are reported as null for any other sources.
-TRAFFIC_SOURCES_SHA256 = "407ec7db1551b16c1055501ad2cb7c8d42f4f13789edbf6c01b2588754c056f8"
+TRAFFIC_SOURCES_SHA256 = "d4cd6ce44f96d6d0c598991c4af6b1e57ef80239c0fb7b8dee192d5b8936c4fc"
 TRAFFIC_BYTES = {
-    "llama8b-prefill-1024q-9216k-r16": 125446774,
-    "decode-64x16384-r16": 4420061837,
-    "decode-shared-16x4x16384-r16": 1165389209,
-    "lr-precompute-32768x4096-3x64": 293974720,
-    "lr-append-64x4096-4x16": 1652098,
-    "longctx-prefill-512q-32768k-r64": 244838635,
+    "llama8b-prefill-1024q-9216k-r16": 125446941,
+    "decode-64x16384-r16": 4416378039,
+    "decode-shared-16x4x16384-r16": 1165177312,
+    "lr-precompute-32768x4096-3x64": 293975077,
+    "lr-append-64x4096-4x16": 1652101,
+    "longctx-prefill-512q-32768k-r64": 244838952,
 }
 
 

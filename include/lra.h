@@ -66,6 +66,9 @@ enum lra_dtype { LRA_DTYPE_F32 = 0, LRA_DTYPE_BF16 = 1 };
 #define LRA_MAX_RANK 64        /* r_a <= 64 and r_a % 8 == 0 (r_a == 0 means no adapter)      */
 #define LRA_MAX_GROUP 8        /* n_q_heads / n_kv_heads                                    */
 #define LRA_MAX_BATCH 1024     /* requests per call                                          */
+/* bf16 attention also needs 64 K/V rows (n_kv_heads * head_dim * 2 bytes each) and 64 rows
+ * of each LR cache (ldl[a] * 2 bytes each) to stay below 2 GiB: tiles are addressed with
+ * 32-bit byte offsets. */
 
 /*
  * lra_precompute_lr -- PreLRShared LR precompute (PReCache abstract, English text on the

@@ -74,6 +74,11 @@ int check_shape(const AttnShape& s) {
   if (s.D <= 0) return fail(LRA_ERR_INVALID, "head_dim %d <= 0", s.D);
   if (s.D != 64 && s.D != 128)
     return fail(LRA_ERR_UNSUPPORTED, "head_dim %d not in {64, 128}", s.D);
+  // the bf16 kernels address a 64-row tile of K/V rows (and B's rank rows) with 32-bit
+  // byte offsets
+  if (s.dtype == LRA_DTYPE_BF16 && (int64_t)s.Hkv * s.D * 2 * 64 >= ((int64_t)1 << 31))
+    return fail(LRA_ERR_UNSUPPORTED, "bf16 K/V rows of %lld bytes: 64 of them must stay below "
+                "2 GiB", (long long)s.Hkv * s.D * 2);
   return LRA_OK;
 }
 
@@ -106,6 +111,10 @@ int check_adapters(int dtype, const Adapters& ad, int64_t kv_rows) {
     if (ad.ldl[a] % ldl_mult != 0)
       return fail(LRA_ERR_INVALID, "ldl[%d] = %lld is not a multiple of %d elements", a,
                   (long long)ad.ldl[a], ldl_mult);
+    // the bf16 kernels address a 64-row tile of LR rows with 32-bit byte offsets
+    if (dtype == LRA_DTYPE_BF16 && ad.ldl[a] * 2 * 64 >= ((int64_t)1 << 31))
+      return fail(LRA_ERR_UNSUPPORTED, "ldl[%d] = %lld: 64 bf16 LR rows must stay below 2 GiB",
+                  a, (long long)ad.ldl[a]);
     if (!aligned(ad.L[a], 16) || !aligned(ad.B[a], 16))
       return fail(LRA_ERR_INVALID, "L[%d] / B[%d] not 16-byte aligned", a, a);
     (void)kv_rows;

@@ -103,6 +103,11 @@ UNSUPPORTED_CASES = {
     "17 agents": (lambda c: setattr(c, "ranks", [8] * 17) or setattr(c, "L", [FAKE] * 17)
                   or setattr(c, "B", [FAKE] * 17) or setattr(c, "ldl", [8] * 17), "LRA_MAX_AGENTS"),
     "batch 2000": (lambda c: setattr(c, "batch", 2000), "LRA_MAX_BATCH"),
+    # 64 bf16 rows of K/V (n_kv_heads * head_dim * 2 bytes each) or of an LR cache must stay
+    # below 2 GiB: the kernels address a tile with 32-bit byte offsets
+    "K/V rows of 32 MiB": (lambda c: setattr(c, "Hq", 1 << 17) or setattr(c, "Hkv", 1 << 17),
+                           "2 GiB"),
+    "LR rows of 32 MiB": (lambda c: c.ldl.__setitem__(0, 1 << 24), "2 GiB"),
 }
 
 
