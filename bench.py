@@ -522,6 +522,48 @@ def environment():
     return env
 
 
+def bench_sdpa_context(steps, warmup):
+    """Context only, not part of the default line: torch's scaled_dot_product_attention with
+    the flash backend forced (it raises rather than falling back to another backend), beside
+    lra_attn_prefill at ranks 0 and 16, on square causal problems of n tokens with 32 q heads
+    and head_dim 128.  SDPA gets 32 kv heads, the lra calls 8 (GQA): the same FLOP.  Calls run
+    back to back, as for the headline."""
+    import torch
+    import torch.nn.functional as F
+    from shared_rank_kv_amd import accounting, workloads
+    rows = []
+    for n in (4096, 9216):
+        row = {"n": n, "flop_rank0": 4 * 128 * (n * (n + 1) // 2) * 32}
+        try:
+            from torch.nn.attention import SDPBackend, sdpa_kernel
+            g = torch.Generator(device="cuda").manual_seed(n)
+            q, k, v = (torch.randn(1, 32, n, 128, dtype=torch.bfloat16, device="cuda",
+                                   generator=g) for _ in range(3))
+            with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+                fn = lambda: F.scaled_dot_product_attention(q, k, v, is_causal=True)  # noqa: E731
+                settle(fn)
+                per, _ = time_calls(fn, steps, warmup)
+            ms = float(np.median(per))
+            row["sdpa_flash"] = {"ms": round(ms, 4),
+                                 "TFLOP/s": round(row["flop_rank0"] / ms / 1e9, 1)}
+            del q, k, v
+        except Exception as ex:  # noqa: BLE001  (no flash kernel for this part)
+            row["sdpa_flash"] = {"error": str(ex)[:200]}
+        for r in (0, 16):
+            prob = workloads.custom(f"square-{n}-r{r}", "bf16", 32, 8, 128, (r,), [n], [n], [0],
+                                    seed=900 + n + r)
+            _, dev = upload(prob)
+            fn = prefill_call(prob, dev, workspace_for(prob, False))
+            settle(fn)
+            per, _ = time_calls(fn, steps, warmup)
+            ms = float(np.median(per))
+            flop, _ = accounting.attention_work(prob)
+            row[f"lra_rank{r}"] = {"ms": round(ms, 4), "TFLOP/s": round(flop / ms / 1e9, 1)}
+            del dev
+        rows.append(row)
+    return {"workload": "square causal prefill, 32 q heads, head_dim 128", "rows": rows}
+
+
 def run_only(args):
     if args.only == "copy":
         import torch
@@ -539,6 +581,8 @@ def run_only(args):
         return bench_append(args.steps, args.warmup, Flusher())
     if args.only == "tiny":
         return bench_tiny_fp32(args.steps, args.warmup)
+    if args.only == "sdpa":
+        return bench_sdpa_context(args.steps, args.warmup)
     if args.only == "naive":
         return bench_naive_expansion(args.steps, args.warmup, Flusher())
     if args.only == "longctx":
@@ -556,9 +600,10 @@ def main():
                     help="time the 32-layer mixed batch (the default; kept for old command lines)")
     ap.add_argument("--no-mixed", action="store_true", help="skip the 32-layer mixed batch")
     ap.add_argument("--only", choices=["prefill", "tiny", "decode", "decode_shared", "append",
-                                       "longctx", "naive", "mixed", "copy"],
+                                       "longctx", "naive", "mixed", "copy", "sdpa"],
                     help="time one workload only (for profiling); prints its JSON object. "
-                         "'copy' times a 1 GiB device copy, the reference for HBM counters")
+                         "'copy' times a 1 GiB device copy, the reference for HBM counters; "
+                         "'sdpa' times torch's flash attention beside the prefill (context)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
