@@ -4,7 +4,10 @@ Each case draws head_dim, the GQA group, the kv heads, 1-6 agents with ranks 0-6
 requests over 1-4 shared contexts (each request reads a prefix of its context, so agents
 that share a context see different lengths of it), empty and ragged query counts, and LR
 caches that are column views of wider buffers whose padding holds NaN.  Decode cases take
-the shared-context grouping path wherever requests share a first base row."""
+the shared-context grouping path wherever requests share a first base row.  Each case runs
+the regrouped route and the in-tile expansion comparator (which expands V tiles in LDS and
+does not group requests); the naive route needs non-overlapping spans per agent and is
+covered by the comparator tests."""
 
 import numpy as np
 import pytest
@@ -71,12 +74,23 @@ def _describe(prob, wide):
 
 @pytest.mark.parametrize("seed", range(40))
 @pytest.mark.parametrize("decode", [False, True], ids=["prefill", "decode"])
-def test_random_shapes(seed, decode):
+@pytest.mark.parametrize("route", ["regrouped", "in_tile"])
+def test_random_shapes(route, decode, seed):
+    from shared_rank_kv_amd import lra
     prob, wide, pads = _random_problem(5000 + seed + (1000 if decode else 0), decode)
-    print(_describe(prob, wide), flush=True)
+    print(f"{route} {_describe(prob, wide)}", flush=True)
     cpu, dev = H.device_inputs(prob)
     _widen(dev, prob, wide, pads)
-    O = H.run_decode(prob, dev) if decode else H.run_prefill(prob, dev)
+    if route == "regrouped":
+        O = H.run_decode(prob, dev) if decode else H.run_prefill(prob, dev)
+    elif decode:
+        O = lra.lra_attn_decode_expand(dev["Q"], dev["K"], dev["V"], dev["L"], dev["B"],
+                                       prob.k_start, prob.k_len, prob.agent_idx)
+    else:
+        O = lra.lra_attn_prefill_expand(dev["Q"], dev["K"], dev["V"], dev["L"], dev["B"],
+                                        prob.q_start, prob.q_len, prob.k_start, prob.k_len,
+                                        prob.agent_idx)
+    torch.cuda.synchronize()
     rows = H.covered_rows(prob)
     if len(rows) == 0:
         return
