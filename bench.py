@@ -122,14 +122,14 @@ def time_calls(fn, steps, warmup, flush=None):
 # what the same counter reads for a plain 1 GiB device copy); the per-kernel summaries and
 # the commands are under profiles/.  The figures describe the kernels built from sources
 # with this digest and are reported as null for any other sources.
-TRAFFIC_SOURCES_SHA256 = "d4cd6ce44f96d6d0c598991c4af6b1e57ef80239c0fb7b8dee192d5b8936c4fc"
+TRAFFIC_SOURCES_SHA256 = "8a0a8b7a2b4f4913477a2ab1d7e9b7ffe77b95682309a27a0dd836c3c5eaed56"
 TRAFFIC_BYTES = {
-    "llama8b-prefill-1024q-9216k-r16": 125446941,
-    "decode-64x16384-r16": 4416378039,
-    "decode-shared-16x4x16384-r16": 1165177312,
-    "lr-precompute-32768x4096-3x64": 293975077,
-    "lr-append-64x4096-4x16": 1652101,
-    "longctx-prefill-512q-32768k-r64": 244838952,
+    "llama8b-prefill-1024q-9216k-r16": 125446549,
+    "decode-64x16384-r16": 4418541634,
+    "decode-shared-16x4x16384-r16": 1164516375,
+    "lr-precompute-32768x4096-3x64": 293973223,
+    "lr-append-64x4096-4x16": 1652094,
+    "longctx-prefill-512q-32768k-r64": 244838087,
 }
 
 

@@ -219,9 +219,9 @@ __global__ __launch_bounds__(256, 1) void lr_precompute_bf16(const PrecomputeArg
     for (int st = 0; st < UNROLL; ++st) {
       const int kc = kc0 + st;
       const LDS char* at = tiles[st % NT];
-      // loads first, so that they are in flight during this step's MFMAs: the tile of chunk
-      // kc - 1 and the X slots of chunks kc - 4 .. kc - 1 are free (the barrier that ended
-      // step kc - 1 follows every read of them)
+      // this step's loads, into the tile of chunk kc - 1 and the X slot of chunk kc - 4, both
+      // free (the barrier that ended step kc - 1 follows every read of them).  The compiler
+      // places them after the MFMAs, just before the wait; keeping them ahead was slower.
       load_a(tiles[(st + NT - 1) % NT], kc + NT - 1);
       load_x(xop[(st + NT) % UNROLL], kc + NT);
 #pragma unroll
